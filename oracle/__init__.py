@@ -1,0 +1,44 @@
+"""CPU oracle for AB-Attention's block-sparse attention path.
+
+TEST INFRASTRUCTURE ONLY. Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import this package; the library under
+``block_sparse_attention_ibcs_amd`` never does, and it shares no code with it.
+
+What it computes follows the AB-Attention abstract (paperdot search page,
+query "Xing Ma"): dynamic block-sparse attention that computes exact attention
+only on key/value blocks selected from the current activations (problem
+sentence), scored by clustering queries inside each query block without
+permuting tokens (IBCS sentence), sampled in proportion to those scores and
+reweighted by the inverse inclusion probability so one pass estimates dense
+attention (SIP sentence). The pages give no formulas; every constant and rule
+the abstract leaves open is a stated reading, listed in the module that uses it.
+
+Precision: k-means is an exact-operation fp32 specification (both sides must
+produce identical bits), the sampler is integer arithmetic on fp32 scores, and
+everything else is float64.
+
+Pins (what fixes each function against something other than itself) live in
+``tests/test_oracle_*.py``. No function here is "parity unpinned".
+"""
+
+from .philox import philox4x32_10
+from .ibcs import kmeans_fp32, block_scores, round_bf16
+from .sip import quantize_scores, budget, inclusion_thresholds, sample_rows, SIP_ONE
+from .attention import dense_attention, sparse_ht_attention
+from .pipeline import Params, run_blocks
+
+__all__ = [
+    "philox4x32_10",
+    "kmeans_fp32",
+    "block_scores",
+    "round_bf16",
+    "quantize_scores",
+    "budget",
+    "inclusion_thresholds",
+    "sample_rows",
+    "SIP_ONE",
+    "dense_attention",
+    "sparse_ht_attention",
+    "Params",
+    "run_blocks",
+]
