@@ -1,0 +1,62 @@
+// Internal declarations shared by the HIP sources of libabattn (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ab_attn.h"
+
+namespace ab {
+
+// Element type tags.
+struct bf16_t {
+  uint16_t bits;
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// Round-to-nearest-even fp32 -> bf16 (inputs are finite in every use here).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+__host__ __device__ constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Derived sizes of one problem.
+struct Dims {
+  int B, H, N, d, Bq, Bk, C, T;
+  int nqb, nkb, mrows;  // query blocks, key sub-blocks, centroid rows per head (nqb*C)
+  float scale;
+  bool bf16;
+};
+
+// Workspace carve-up of ab_score (byte offsets, 256-byte aligned).
+struct ScoreWs {
+  size_t centroids_f32;  // fp32 [B,H,nqb,C,d]
+  size_t centroids_bf16; // bf16 [B,H,nqb,C,d]
+  size_t sizes;          // int32 [B,H,nqb,C]
+  size_t ell;            // fp32 [B,H,nqb,nkb,C]: base-2 log-sum-exp of each (block, sub-block, cluster)
+  size_t lpart;          // fp32 [B,H,nqb*C,splits]: base-2 log-sum-exp of each row over one key split
+  size_t total;
+  int splits;            // key splits of the scorer GEMM
+  int split_keys;        // keys per split (multiple of 128)
+};
+
+ScoreWs score_ws_layout(const Dims& D, int num_cus);
+
+// Launchers: return hipSuccess or the launch error.
+hipError_t launch_kmeans(const Dims& D, const void* q, float* centroids, uint16_t* centroids_bf16,
+                         int32_t* sizes, uint8_t* assign, hipStream_t s);
+hipError_t launch_score_lse(const Dims& D, const ScoreWs& L, const void* k, const void* cent_any,
+                            float* ell, float* lpart, hipStream_t s);
+hipError_t launch_score_assemble(const Dims& D, const ScoreWs& L, const float* ell, const float* lpart,
+                                 const int32_t* sizes, float* scores, hipStream_t s);
+hipError_t launch_sample(const Dims& D, const float* scores, int K, uint64_t seed, int32_t* idx,
+                         float* weights, int32_t* counts, uint32_t* mask, hipStream_t s);
+hipError_t launch_attn_fwd(const Dims& D, const void* q, const void* k, const void* v, const int32_t* idx,
+                           const float* weights, const int32_t* counts, void* out, float* lse,
+                           hipStream_t s);
+
+}  // namespace ab

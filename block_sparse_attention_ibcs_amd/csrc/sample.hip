@@ -1,0 +1,216 @@
+// SIP: sampling with inclusion-probability weighting (AB-Attention abstract,
+// SIP sentence), integer-exact given the fp32 scores.
+//
+// Per row (b, h, i) of the score matrix:
+//   w_j = max(1, floor(s_j * 2^24))          (NaN or s <= 0 -> 1, s >= 1 -> 2^24)
+//   water-filling: grow a capped set while some uncapped j has (K - m) w_j >= S
+//   (m = capped count, S = uncapped weight total); thresholds t_j = 2^24 when
+//   capped, else max(1, floor((K - m) w_j 2^24 / S)); inclusion prob = t_j / 2^24
+//   u_j = word (j mod 4) of Philox4x32-10(key = seed, counter = (j/4, i, h, b)) >> 8
+//   keep iff u_j < t_j; weight = fp32(2^24) / fp32(t_j)
+// Philox4x32-10 follows Salmon et al., SC'11.
+//
+// One workgroup per row. The capped set is an LDS bitset; each pass is one
+// workgroup reduction of a 64-bit sum. The draw gives each thread one 32-block
+// word of the mask (eight Philox calls), and a workgroup exclusive scan of the
+// per-word popcounts places the kept indices in ascending order.
+#include "ab_internal.h"
+
+namespace ab {
+namespace {
+
+constexpr uint32_t kOne = 1u << 24;
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ uint32_t quantize(float s) {
+  if (!(s > 0.0f)) return 1u;        // NaN, zero, negative
+  if (s >= 1.0f) return kOne;
+  const float v = s * 16777216.0f;   // exact
+  const uint32_t q = uint32_t(v);    // truncation == floor for v >= 0
+  return q > 0u ? q : 1u;
+}
+
+__device__ __forceinline__ void philox_round(uint32_t& c0, uint32_t& c1, uint32_t& c2, uint32_t& c3, uint32_t k0,
+                                             uint32_t k1) {
+  const uint64_t p0 = uint64_t(0xD2511F53u) * c0;
+  const uint64_t p1 = uint64_t(0xCD9E8D57u) * c2;
+  const uint32_t hi0 = uint32_t(p0 >> 32), lo0 = uint32_t(p0);
+  const uint32_t hi1 = uint32_t(p1 >> 32), lo1 = uint32_t(p1);
+  const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+  c0 = n0;
+  c1 = lo1;
+  c2 = n2;
+  c3 = lo0;
+}
+
+__device__ __forceinline__ uint4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
+                                               uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r > 0) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    philox_round(c0, c1, c2, c3, k0, k1);
+  }
+  return make_uint4(c0, c1, c2, c3);
+}
+
+template <typename T>
+__device__ __forceinline__ T block_sum(T v, T* red) {
+  // wave reduction then across the four waves
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  const int wave = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  __syncthreads();
+  T t = red[0];
+  for (int w = 1; w < kThreads / 64; ++w) t += red[w];
+  return t;
+}
+
+// floor(num / den) for num < 2^62, den < 2^40, via one fp64 division and an exact fix-up.
+__device__ __forceinline__ uint64_t udiv_floor(uint64_t num, uint64_t den) {
+  uint64_t q = uint64_t(double(num) / double(den));
+  while (q * den > num) --q;
+  while ((q + 1) * den <= num) ++q;
+  return q;
+}
+
+__global__ __launch_bounds__(kThreads) void sample_kernel(Dims P, int K, uint32_t seed_lo, uint32_t seed_hi,
+                                                          const float* __restrict__ scores,
+                                                          int32_t* __restrict__ idx, float* __restrict__ weights,
+                                                          int32_t* __restrict__ counts,
+                                                          uint32_t* __restrict__ mask) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int nkb = P.nkb;
+  const int words = ceil_div(nkb, 32);
+  uint32_t* capped = reinterpret_cast<uint32_t*>(smem);  // [words]
+  __shared__ uint64_t red64[4];
+  __shared__ int red32[4];
+  __shared__ int scan_base;
+  __shared__ int wave_tot[4];
+
+  const int row = blockIdx.x;  // (b*H + h)*nqb + i
+  const int i = row % P.nqb;
+  const int bh = row / P.nqb;
+  const int h = bh % P.H, b = bh / P.H;
+  const float* s = scores + size_t(row) * nkb;
+  const int tid = threadIdx.x;
+
+  const bool all = (K >= nkb);
+  for (int w = tid; w < words; w += kThreads) {
+    uint32_t v = 0;
+    if (all) {
+      const int rem = nkb - w * 32;
+      v = rem >= 32 ? 0xFFFFFFFFu : ((1u << rem) - 1u);
+    }
+    capped[w] = v;
+  }
+  __syncthreads();
+
+  // ---- integer water-filling ----
+  uint64_t room = 0, S = 1;
+  if (!all) {
+    int m = 0;
+    for (;;) {
+      uint64_t part = 0;
+      for (int j = tid; j < nkb; j += kThreads)
+        if (!((capped[j >> 5] >> (j & 31)) & 1u)) part += quantize(s[j]);
+      S = block_sum<uint64_t>(part, red64);
+      room = uint64_t(K - m);
+      __syncthreads();
+      int nnew = 0;
+      for (int j = tid; j < nkb; j += kThreads) {
+        if (!((capped[j >> 5] >> (j & 31)) & 1u)) {
+          if (room * quantize(s[j]) >= S) {
+            atomicOr(&capped[j >> 5], 1u << (j & 31));
+            ++nnew;
+          }
+        }
+      }
+      nnew = block_sum<int>(nnew, red32);
+      __syncthreads();
+      if (nnew == 0) break;
+      m += nnew;
+    }
+  }
+
+  // ---- draw, compaction, outputs ----
+  if (tid == 0) scan_base = 0;
+  __syncthreads();
+  const size_t out0 = size_t(row) * nkb;
+  for (int w0 = 0; w0 < words; w0 += kThreads) {
+    const int w = w0 + tid;
+    uint32_t keep = 0;
+    uint32_t tw[32];
+    if (w < words) {
+      const uint32_t cw = capped[w];
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {
+        const int jg = w * 32 + g * 4;
+        if (jg >= nkb) break;
+        const uint4 r = philox4x32_10(uint32_t(jg >> 2), uint32_t(i), uint32_t(h), uint32_t(b), seed_lo, seed_hi);
+        const uint32_t rr[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = jg + e;
+          const int bit = g * 4 + e;
+          tw[bit] = kOne;
+          if (j < nkb) {
+            uint32_t t;
+            if ((cw >> bit) & 1u) {
+              t = kOne;
+            } else {
+              const uint64_t num = room * uint64_t(quantize(s[j])) * uint64_t(kOne);
+              const uint64_t q = udiv_floor(num, S);
+              t = q > 0 ? uint32_t(q) : 1u;
+            }
+            tw[bit] = t;
+            if ((rr[e] >> 8) < t) keep |= 1u << bit;
+          }
+        }
+      }
+      if (mask) mask[size_t(row) * words + w] = keep;
+    }
+    // exclusive scan of popcounts across the workgroup (ascending word order)
+    const int pc = __popc(keep);
+    int incl = pc;
+    const int lane = tid & 63, wave = tid >> 6;
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += y;
+    }
+    if (lane == 63) wave_tot[wave] = incl;
+    __syncthreads();
+    int base = scan_base;
+    for (int wv = 0; wv < wave; ++wv) base += wave_tot[wv];
+    int pos = base + incl - pc;
+    if (w < words) {
+#pragma unroll
+      for (int bit = 0; bit < 32; ++bit) {
+        if ((keep >> bit) & 1u) {
+          idx[out0 + pos] = w * 32 + bit;
+          weights[out0 + pos] = __fdiv_rn(16777216.0f, float(tw[bit]));
+          ++pos;
+        }
+      }
+    }
+    __syncthreads();
+    if (tid == kThreads - 1) scan_base = base + incl;
+    __syncthreads();
+  }
+  if (tid == 0) counts[row] = scan_base;
+}
+
+}  // namespace
+
+hipError_t launch_sample(const Dims& P, const float* scores, int K, uint64_t seed, int32_t* idx, float* weights,
+                         int32_t* counts, uint32_t* mask, hipStream_t s) {
+  const size_t lds = size_t(ceil_div(P.nkb, 32)) * 4;
+  hipLaunchKernelGGL(sample_kernel, dim3(P.B * P.H * P.nqb), dim3(kThreads), lds, s, P, K, uint32_t(seed),
+                     uint32_t(seed >> 32), scores, idx, weights, counts, mask);
+  return hipGetLastError();
+}
+
+}  // namespace ab

@@ -1,0 +1,178 @@
+/*
+ * ab_attn.h - C ABI of the MI355X (gfx950) block-sparse attention library.
+ *
+ * The library implements the three stages of AB-Attention as described in the
+ * AB-Attention abstract (paperdot search page, query "Xing Ma"):
+ *
+ *   ab_score     IBCS sentence: per-query-block k-means of the queries (tokens
+ *                stay in place) and a block-importance estimate for every
+ *                (query block, key sub-block) pair.
+ *   ab_sample    SIP sentence: sample key sub-blocks in proportion to the
+ *                estimates and weight each kept block by the inverse of its
+ *                inclusion probability.
+ *   ab_attn_fwd  kernel sentence + problem sentence: exact attention restricted
+ *                to the kept sub-blocks, gathering sub-blocks smaller than a
+ *                matrix-core tile into full tiles, with the inverse-probability
+ *                weights applied to numerator and denominator of the softmax.
+ *
+ * Conventions shared by every entry point:
+ *
+ * - Tensors. q, k, v and out are contiguous [B, H, N, d] row-major arrays in
+ *   the descriptor's dtype, with token n = (t*Hg + y)*W + x of the video latent
+ *   (raster order, never permuted). Query block i covers rows
+ *   [i*q_block, min(N, (i+1)*q_block)); key sub-block j covers keys
+ *   [j*k_block, min(N, (j+1)*k_block)). NQB = ceil(N/q_block),
+ *   NKB = ceil(N/k_block).
+ * - Memory. Every tensor pointer is a DEVICE pointer owned by the caller. The
+ *   library allocates no device memory and keeps no state besides a
+ *   thread-local error string; scratch space is the caller's workspace.
+ * - Streams. `stream` is a hipStream_t (NULL = the default stream). Calls only
+ *   enqueue work and return; inputs and outputs must stay alive until the
+ *   stream has drained. Outputs are deterministic run to run (no floating-point
+ *   atomics).
+ * - Errors. Every call validates its arguments on the host before enqueuing
+ *   anything and returns 0 or one of the negative AB_ERR_* codes below;
+ *   ab_last_error() then holds a thread-local description. Nothing aborts.
+ */
+#ifndef AB_ATTN_H
+#define AB_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define AB_ABI_VERSION 1
+
+/* Return codes. */
+#define AB_OK 0
+#define AB_ERR_NULL (-1)      /* a required pointer is NULL */
+#define AB_ERR_SHAPE (-2)     /* B, H, N < 1, d not in {64, 128}, or sizes overflow */
+#define AB_ERR_PARAM (-3)     /* q_block, k_block, n_clusters or kmeans_iters out of range */
+#define AB_ERR_DENSITY (-4)   /* density not in (0, 1] (NaN included) */
+#define AB_ERR_DTYPE (-5)     /* dtype is not AB_BF16 or AB_F32 */
+#define AB_ERR_WORKSPACE (-6) /* workspace smaller than ab_score_workspace_size() */
+#define AB_ERR_HIP (-7)       /* a HIP runtime call or kernel launch failed */
+#define AB_ERR_DEVICE (-8)    /* the current device is not gfx950 */
+
+/* Element types of q, k, v and out. */
+#define AB_BF16 0
+#define AB_F32 1
+
+/* Problem descriptor shared by all calls. */
+typedef struct ab_desc {
+  int32_t B, H, N, d;   /* batch, heads, tokens, head dim (d in {64, 128}) */
+  int32_t dtype;        /* AB_BF16 or AB_F32 */
+  int32_t q_block;      /* query block rows Bq, 64 or 128 */
+  int32_t k_block;      /* key sub-block Bk, one of 16, 32, 64, 128 */
+  int32_t n_clusters;   /* C, 1 <= C <= q_block; a block with n_i < C uses n_i */
+  int32_t kmeans_iters; /* T, 1 <= T <= 64: Lloyd iterations per query block */
+  float scale;          /* softmax scale; <= 0 means 1/sqrt(d) */
+} ab_desc;
+
+/* Library version of this header (AB_ABI_VERSION). */
+int32_t ab_abi_version(void);
+
+/* Static text for a return code. */
+const char* ab_status_str(int32_t code);
+
+/* Thread-local description of the last failure on this thread ("" if none). */
+const char* ab_last_error(void);
+
+/*
+ * Bytes of device workspace ab_score needs for this descriptor, or 0 when the
+ * descriptor is invalid (ab_last_error says why). Covers the k-means
+ * centroids (fp32 and bf16 copies), cluster sizes, the per (query block,
+ * key sub-block, cluster) log-sum-exp table and the per-split partial
+ * log-sum-exps. The workspace must be 256-byte aligned.
+ */
+size_t ab_score_workspace_size(const ab_desc* desc);
+
+/*
+ * IBCS block-importance estimates (AB-Attention abstract, IBCS sentence).
+ *
+ * For each query block (b, h, i): k-means with C clusters and T iterations on
+ * the block's queries (exact-operation fp32: left-to-right distance sums with
+ * separate multiply and add, ties to the lowest cluster, members summed in
+ * ascending row order, one correctly rounded division; strided initial
+ * centroids; empty clusters keep their centroid with size 0), then
+ *   scores[b,h,i,j] = sum_c (n_c/n_i) * exp(l_cj - L_c),
+ *   l_cj = log sum_{k in sub-block j} exp(scale * mu_c . k_k),  L_c = log sum_j exp(l_cj),
+ * with mu_c rounded to bf16 before the product for bf16 inputs. Each score row
+ * sums to 1 (up to rounding).
+ *
+ * q, k:    device [B, H, N, d], dtype of desc.
+ * scores:  device fp32 [B, H, NQB, NKB], written in full.
+ * ws:      device workspace of ws_bytes >= ab_score_workspace_size(desc),
+ *          256-byte aligned; its contents are scratch.
+ */
+int32_t ab_score(const ab_desc* desc, const void* q, const void* k, float* scores,
+                 void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The k-means stage of ab_score on its own, with every intermediate exposed
+ * (the clustering of the IBCS sentence).
+ *
+ * centroids: device fp32 [B, H, NQB, C, d] (clusters c >= n_i are zero);
+ * sizes:     device int32 [B, H, NQB, C];
+ * assign:    device uint8 [B, H, N], cluster of each query after the last
+ *            assignment step. Any of the three may be NULL (not written), but
+ *            not all of them.
+ */
+int32_t ab_score_debug(const ab_desc* desc, const void* q, float* centroids, int32_t* sizes,
+                       uint8_t* assign, void* stream);
+
+/*
+ * SIP sampling (AB-Attention abstract, SIP sentence), integer-exact given the
+ * fp32 scores.
+ *
+ * Per row (b, h, i): w_j = max(1, floor(s_j * 2^24)) (NaN or s <= 0 -> 1,
+ * s >= 1 -> 2^24); budget K = clamp(floor(density*NKB + 0.5), 1, NKB) in fp64;
+ * thresholds t_j in [1, 2^24] by integer water-filling (inclusion probability
+ * t_j/2^24 proportional to w_j, capped at 1, summing to K up to floors);
+ * u_j = word (j mod 4) of Philox4x32-10(key = (seed mod 2^32, seed >> 32),
+ * counter = (floor(j/4), i, h, b)) >> 8; block j is kept iff u_j < t_j, with
+ * weight fp32(2^24)/fp32(t_j).
+ *
+ * scores:    device fp32 [B, H, NQB, NKB].
+ * idx:       device int32 [B, H, NQB, NKB]; the first counts[row] entries of a
+ *            row hold the kept sub-block indices in ascending order; the rest
+ *            is left untouched.
+ * weights:   device fp32 [B, H, NQB, NKB], aligned with idx.
+ * counts:    device int32 [B, H, NQB].
+ * mask_bits: device uint32 [B, H, NQB, ceil(NKB/32)], bit j%32 of word j/32
+ *            set iff block j is kept; may be NULL.
+ */
+int32_t ab_sample(const ab_desc* desc, const float* scores, double density, uint64_t seed,
+                  int32_t* idx, float* weights, int32_t* counts, uint32_t* mask_bits,
+                  void* stream);
+
+/*
+ * Weighted block-sparse attention forward (AB-Attention abstract, problem,
+ * SIP and kernel sentences).
+ *
+ * For every query row r of block i of (b, h), over the kept sub-blocks j of
+ * row (b, h, i) with weights w_j:
+ *   den_r = sum_j w_j sum_{k in j} exp(scale*q_r.k_k - m_r),
+ *   out_r = (sum_j w_j sum_{k in j} exp(scale*q_r.k_k - m_r) v_k) / den_r,
+ *   lse_r = m_r + log(den_r);
+ * a block that keeps nothing gives out = 0 and lse = -inf. Sub-blocks smaller
+ * than the kernel's key tile are packed together into one tile.
+ *
+ * q, k, v: device [B, H, N, d], dtype of desc.
+ * idx, weights, counts: as written by ab_sample (indices must be ascending,
+ *            unique and in [0, NKB); counts in [0, NKB]).
+ * out:     device [B, H, N, d], dtype of desc.
+ * lse:     device fp32 [B, H, N] natural-log log-sum-exp; may be NULL.
+ */
+int32_t ab_attn_fwd(const ab_desc* desc, const void* q, const void* k, const void* v,
+                    const int32_t* idx, const float* weights, const int32_t* counts,
+                    void* out, float* lse, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AB_ATTN_H */

@@ -1,0 +1,124 @@
+"""Host-side checks of the C ABI: the library loads, exports every function the
+header declares, sizes workspaces, and rejects bad arguments before touching
+the GPU (no compute calls here; these run without a GPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_sparse_attention_ibcs_amd as ab
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ab_attn.h")
+
+
+def _lib():
+    try:
+        return ab.load_library()
+    except ImportError as e:
+        pytest.fail(f"libabattn.so not built: {e}")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ab_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_expected_entry_points():
+    assert set(_declared_functions()) == set(ab.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib()
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    assert lib.ab_abi_version() == 1
+
+
+def test_status_strings():
+    lib = _lib()
+    for code in range(0, -9, -1):
+        assert lib.ab_status_str(code)
+    assert lib.ab_status_str(-99) == b"unknown status"
+
+
+def _desc(**kw):
+    base = dict(B=1, H=12, N=32760, d=128, dtype=ab.AB_BF16, q_block=128, k_block=32, n_clusters=8, kmeans_iters=4)
+    base.update(kw)
+    return ab.Desc(**base)
+
+
+def test_workspace_size_covers_tables():
+    d = _desc()
+    n = ab.ab_score_workspace_size(d)
+    heads = 12
+    nqb, nkb = 256, 1024
+    ell = heads * nqb * nkb * 8 * 4
+    cent = heads * nqb * 8 * 128 * (4 + 2)
+    assert n >= ell + cent
+    assert n < ell + cent + 64 * 1024 * 1024  # the partial tables are small
+
+
+@pytest.mark.parametrize(
+    "kw,code",
+    [
+        (dict(d=96), -2),
+        (dict(N=0), -2),
+        (dict(B=0), -2),
+        (dict(dtype=7), -5),
+        (dict(q_block=32), -3),
+        (dict(k_block=48), -3),
+        (dict(k_block=256), -3),
+        (dict(n_clusters=0), -3),
+        (dict(n_clusters=129), -3),
+        (dict(kmeans_iters=0), -3),
+        (dict(kmeans_iters=65), -3),
+        (dict(N=1 << 25), -2),
+    ],
+)
+def test_validation_errors(kw, code):
+    lib = _lib()
+    cd = _desc(**kw).c()
+    assert lib.ab_score_workspace_size(ctypes.byref(cd)) == 0
+    fake = ctypes.c_void_p(256)
+    rc = lib.ab_score(ctypes.byref(cd), fake, fake, fake, fake, 1 << 40, None)
+    assert rc == code
+    assert lib.ab_last_error()
+    rc = lib.ab_attn_fwd(ctypes.byref(cd), fake, fake, fake, fake, fake, fake, fake, None, None)
+    assert rc == code
+
+
+def test_null_and_workspace_errors():
+    lib = _lib()
+    cd = _desc().c()
+    fake = ctypes.c_void_p(256)
+    need = lib.ab_score_workspace_size(ctypes.byref(cd))
+    assert lib.ab_score(None, fake, fake, fake, fake, need, None) == -1
+    assert lib.ab_score(ctypes.byref(cd), None, fake, fake, fake, need, None) == -1
+    assert lib.ab_score(ctypes.byref(cd), fake, fake, fake, fake, need - 1, None) == -6
+    assert b"workspace" in lib.ab_last_error()
+    assert lib.ab_score(ctypes.byref(cd), fake, fake, fake, ctypes.c_void_p(256 + 16), need, None) == -6
+    assert lib.ab_attn_fwd(ctypes.byref(cd), fake, fake, None, fake, fake, fake, fake, None, None) == -1
+    assert lib.ab_score_debug(ctypes.byref(cd), fake, None, None, None, None) == -1
+
+
+@pytest.mark.parametrize("density", [0.0, -0.5, 1.0000001, float("nan"), float("inf")])
+def test_density_errors(density):
+    lib = _lib()
+    cd = _desc().c()
+    fake = ctypes.c_void_p(256)
+    rc = lib.ab_sample(ctypes.byref(cd), fake, ctypes.c_double(density), 0, fake, fake, fake, None, None)
+    assert rc == -4
+    assert b"density" in lib.ab_last_error()
+
+
+def test_python_binding_rejects_host_tensors():
+    import torch
+
+    d = _desc(H=1, N=256, d=64, dtype=ab.AB_F32, q_block=64, k_block=16, n_clusters=4)
+    q = torch.zeros(1, 1, 256, 64)
+    with pytest.raises(ValueError):
+        ab.ab_score(d, q, q, workspace=torch.zeros(16, dtype=torch.uint8))

@@ -1,0 +1,338 @@
+"""GPU parity: every stage of the HIP path against the CPU oracle, through the C ABI.
+
+Stage injection: each GPU stage is compared with the oracle stage fed the same
+inputs -
+  k-means (centroids, sizes, assignments): bit-exact;
+  scores: |d| <= 1e-6 + 1e-3*s (bf16) or 1e-6 + 1e-4*s (fp32);
+  sampler run by the oracle on the GPU's own scores: idx, weights, counts and
+  mask bits bit-exact;
+  attention run by the oracle on the GPU's own idx/weights: max-abs <= 2e-2 and
+  relative L2 <= 1e-2 (bf16), max-abs <= 1e-5 (fp32); LSE within 1e-3 (bf16) or
+  1e-5 (fp32) relative to max(1, |LSE|).
+The four video-shaped workloads run at full size in the launch configuration
+the benchmark times; the oracle checks a seeded sample of query blocks that
+always includes the first block and the ragged last one, and properties that
+hold at any size are checked on every row.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_ibcs_amd as ab
+import workloads
+from oracle import Params, dense_attention, kmeans_fp32, block_scores, sample_rows, sparse_ht_attention
+from oracle.sip import SIP_ONE
+
+pytestmark = pytest.mark.gpu
+
+TOL = {
+    "bf16": dict(score_abs=1e-6, score_rel=1e-3, o_abs=2e-2, o_rl2=1e-2, lse=1e-3),
+    "fp32": dict(score_abs=1e-6, score_rel=1e-4, o_abs=1e-5, o_rl2=1e-5, lse=1e-5),
+}
+
+
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def _to_dev(x, dtype):
+    t = torch.from_numpy(x)
+    return t.to(dtype).to("cuda:0") if dtype == torch.bfloat16 else t.to("cuda:0")
+
+
+class Run:
+    """Inputs of one workload on host and device, and the GPU outputs of the whole path."""
+
+    def __init__(self, w, density=None, seed=0, data_seed=0, inputs=None):
+        _gpu()
+        self.w = w
+        self.density = w.density if density is None else density
+        self.seed = seed
+        self.q, self.k, self.v = inputs if inputs is not None else workloads.generate(w, seed=data_seed)
+        tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+        self.qd, self.kd, self.vd = (_to_dev(x, tdt) for x in (self.q, self.k, self.v))
+        self.desc = ab.Desc.for_tensor(self.qd, w.q_block, w.k_block, w.n_clusters, w.kmeans_iters)
+        self.params = Params(w.q_block, w.k_block, w.n_clusters, w.kmeans_iters, self.density, bf16=w.dtype == "bf16")
+        self.scale = 1.0 / math.sqrt(w.d)
+        self.run_gpu()
+
+    def run_gpu(self):
+        d = self.desc
+        self.scores_d = ab.ab_score(d, self.qd, self.kd)
+        self.idx_d, self.wts_d, self.cnt_d, self.mask_d = ab.ab_sample(d, self.scores_d, self.density, self.seed)
+        self.out_d, self.lse_d = ab.ab_attn_fwd(d, self.qd, self.kd, self.vd, self.idx_d, self.wts_d, self.cnt_d)
+        torch.cuda.synchronize()
+        self.scores = self.scores_d.cpu().numpy()
+        self.idx = self.idx_d.cpu().numpy()
+        self.wts = self.wts_d.cpu().numpy()
+        self.cnt = self.cnt_d.cpu().numpy()
+        self.mask = self.mask_d.cpu().numpy().view(np.uint32)
+        self.out = self.out_d.float().cpu().numpy()
+        self.lse = self.lse_d.cpu().numpy()
+
+    def blocks(self, max_blocks=24, rng_seed=7):
+        w = self.w
+        allb = [(b, h, i) for b in range(w.B) for h in range(w.H) for i in range(w.nqb)]
+        if len(allb) <= max_blocks:
+            return allb
+        rng = np.random.default_rng(rng_seed)
+        pick = {0, len(allb) - 1, w.nqb - 1}
+        pick.update(rng.choice(len(allb), size=max_blocks - len(pick), replace=False).tolist())
+        return [allb[t] for t in sorted(pick)]
+
+
+def _rows_of(w, b, h, i):
+    lo = i * w.q_block
+    return lo, min(w.N, lo + w.q_block)
+
+
+def check_kmeans(run, blocks):
+    w = run.w
+    cent, sizes, assign = ab.ab_score_debug(run.desc, run.qd)
+    torch.cuda.synchronize()
+    cent, sizes, assign = cent.cpu().numpy(), sizes.cpu().numpy(), assign.cpu().numpy()
+    for (b, h, i) in blocks:
+        lo, hi = _rows_of(w, b, h, i)
+        mu, sz, a = kmeans_fp32(run.q[b, h, lo:hi], w.n_clusters, w.kmeans_iters)
+        assert np.array_equal(cent[b, h, i].view(np.uint32), mu.view(np.uint32)), (b, h, i)
+        assert np.array_equal(sizes[b, h, i], sz), (b, h, i)
+        assert np.array_equal(assign[b, h, lo:hi], a), (b, h, i)
+
+
+def check_scores(run, blocks):
+    w = run.w
+    tol = TOL[w.dtype]
+    for (b, h, i) in blocks:
+        lo, hi = _rows_of(w, b, h, i)
+        mu, sz, _ = kmeans_fp32(run.q[b, h, lo:hi], w.n_clusters, w.kmeans_iters)
+        ref = block_scores(mu, sz, hi - lo, run.k[b, h], w.k_block, run.scale, w.dtype == "bf16").astype(np.float64)
+        got = run.scores[b, h, i].astype(np.float64)
+        err = np.abs(got - ref)
+        lim = tol["score_abs"] + tol["score_rel"] * np.abs(ref)
+        assert np.all(err <= lim), (b, h, i, float((err / lim).max()))
+    # any size: every score row is a distribution over key sub-blocks
+    sums = run.scores.astype(np.float64).sum(axis=-1)
+    assert np.all(np.abs(sums - 1.0) < 1e-4), float(np.abs(sums - 1).max())
+    assert np.all(run.scores >= 0)
+
+
+def check_sampler(run, rows):
+    ref = sample_rows(run.scores, run.density, run.seed, rows)
+    for key, o in ref.items():
+        b, h, i = key
+        c = int(run.cnt[b, h, i])
+        assert c == o["count"], key
+        assert np.array_equal(run.idx[b, h, i, :c], o["idx"]), key
+        assert np.array_equal(run.wts[b, h, i, :c].view(np.uint32), o["weight"].view(np.uint32)), key
+        assert np.array_equal(run.mask[b, h, i], o["mask"]), key
+
+
+def check_sampler_any_size(run):
+    # counts agree with the mask popcounts and indices are ascending and in range
+    bits = np.unpackbits(run.mask.view(np.uint8), axis=-1, bitorder="little").sum(axis=-1)
+    assert np.array_equal(bits, run.cnt)
+    nkb = run.w.nkb
+    for (b, h, i) in run.blocks(64, rng_seed=3):
+        c = int(run.cnt[b, h, i])
+        ids = run.idx[b, h, i, :c]
+        assert np.all(np.diff(ids) > 0) and (c == 0 or (ids[0] >= 0 and ids[-1] < nkb))
+        assert np.all(run.wts[b, h, i, :c] >= 1.0)
+
+
+def check_attention(run, blocks):
+    w = run.w
+    tol = TOL[w.dtype]
+    worst = 0.0
+    for (b, h, i) in blocks:
+        lo, hi = _rows_of(w, b, h, i)
+        c = int(run.cnt[b, h, i])
+        o_ref, lse_ref = sparse_ht_attention(run.q[b, h, lo:hi], run.k[b, h], run.v[b, h], run.idx[b, h, i, :c],
+                                             run.wts[b, h, i, :c], w.k_block, run.scale)
+        if w.dtype == "bf16":
+            o_ref = torch.from_numpy(o_ref).to(torch.bfloat16).double().numpy()  # the output is rounded to bf16
+        got = run.out[b, h, lo:hi].astype(np.float64)
+        if c == 0:
+            assert np.all(got == 0) and np.all(np.isneginf(run.lse[b, h, lo:hi]))
+            continue
+        err = np.abs(got - o_ref)
+        assert err.max() <= tol["o_abs"], (b, h, i, float(err.max()))
+        rl2 = np.linalg.norm(got - o_ref) / max(np.linalg.norm(o_ref), 1e-30)
+        assert rl2 <= tol["o_rl2"], (b, h, i, rl2)
+        lerr = np.abs(run.lse[b, h, lo:hi] - lse_ref) / np.maximum(1.0, np.abs(lse_ref))
+        assert lerr.max() <= tol["lse"], (b, h, i, float(lerr.max()))
+        worst = max(worst, float(err.max()))
+    return worst
+
+
+_CACHE = {}
+
+
+def _run(name, **kw):
+    key = (name, tuple(sorted(kw.items())))
+    if key not in _CACHE:
+        _CACHE.clear()  # keep at most one large workload resident
+        torch.cuda.empty_cache()
+        _CACHE[key] = Run(workloads.get(name), **kw)
+    return _CACHE[key]
+
+
+# ---------------------------------------------------------------- tiny (fp32)
+
+
+@pytest.mark.parametrize("density", [1.0, 0.25])
+def test_tiny_full_path(density):
+    run = _run("tiny", density=density)
+    blocks = run.blocks()
+    check_kmeans(run, blocks)
+    check_scores(run, blocks)
+    check_sampler(run, blocks)
+    check_sampler_any_size(run)
+    check_attention(run, blocks)
+
+
+def test_tiny_density_one_equals_dense():
+    run = _run("tiny", density=1.0)
+    assert np.all(run.cnt == run.w.nkb)
+    o, lse = dense_attention(run.q[0, 0], run.k[0, 0], run.v[0, 0], run.scale)
+    assert np.abs(run.out[0, 0] - o).max() <= 1e-5
+    assert np.abs(run.lse[0, 0] - lse).max() <= 1e-5
+
+
+def test_tiny_end_to_end_masks_match_oracle():
+    """Independent CPU scores -> CPU sampler against the GPU end to end: no mask flips."""
+    run = _run("tiny", density=0.25)
+    res = __import__("oracle").run_blocks(run.q, run.k, run.v, run.params, run.seed, run.blocks(), with_attention=False)
+    flips = 0
+    for (b, h, i), r in res.items():
+        flips += int(np.unpackbits((r["mask"] ^ run.mask[b, h, i]).view(np.uint8)).sum())
+    assert flips == 0
+
+
+# ------------------------------------------------------- video-shaped (bf16)
+
+
+@pytest.mark.parametrize("name", ["wan1.3b", "wan14b", "hunyuan"])
+def test_video_workload_full_path(name):
+    run = _run(name)
+    blocks = run.blocks(24)
+    check_kmeans(run, blocks)
+    check_scores(run, blocks)
+    rng = np.random.default_rng(11)
+    rows = set(blocks)
+    w = run.w
+    for t in rng.choice(w.B * w.H * w.nqb, size=200, replace=False):
+        rows.add((int(t) // (w.H * w.nqb), (int(t) // w.nqb) % w.H, int(t) % w.nqb))
+    check_sampler(run, sorted(rows))
+    check_sampler_any_size(run)
+    worst = check_attention(run, blocks)
+    # realised density is close to the target (Poisson sampling around K per row)
+    K = max(1, min(w.nkb, math.floor(run.density * w.nkb + 0.5)))
+    assert abs(run.cnt.mean() - K) < 0.05 * K + 1
+    print(f"{name}: worst attention |err| {worst:.3e}, mean kept {run.cnt.mean():.1f} of K={K}")
+
+
+def test_deterministic_outputs():
+    run = _run("wan1.3b")
+    s1, i1, w1, c1, o1 = (t.clone() for t in (run.scores_d, run.idx_d, run.wts_d, run.cnt_d, run.out_d))
+    run.run_gpu()
+    assert torch.equal(s1, run.scores_d)
+    assert torch.equal(c1, run.cnt_d)
+    assert torch.equal(o1, run.out_d)
+
+
+# ------------------------------------------------------------- edge cases
+
+
+EDGE = [
+    # (N, H, d, Bq, Bk, C, T, density)
+    (1000, 2, 128, 128, 32, 8, 4, 0.3),
+    (1000, 2, 128, 128, 16, 8, 2, 0.2),
+    (777, 2, 128, 128, 64, 8, 4, 0.3),
+    (777, 2, 128, 128, 128, 8, 4, 0.5),
+    (1000, 2, 64, 64, 32, 4, 4, 0.3),
+    (1000, 2, 64, 128, 16, 8, 1, 0.15),
+    (900, 1, 128, 128, 32, 1, 3, 0.3),
+    (640, 1, 128, 128, 32, 128, 2, 0.3),
+    (520, 2, 128, 64, 16, 64, 2, 0.25),
+    (1000, 2, 128, 128, 32, 8, 4, 1.0),
+    (130, 1, 128, 128, 128, 8, 4, 0.01),
+    (70, 1, 64, 64, 16, 4, 4, 1.0),
+]
+
+
+@pytest.mark.parametrize("N,H,d,Bq,Bk,C,T,density", EDGE)
+def test_edge_shapes(N, H, d, Bq, Bk, C, T, density):
+    _gpu()
+    w = workloads.Workload("edge", 1, H, (1, 1, N), d, "bf16", Bq, Bk, C, density, 0.5, False, kmeans_iters=T)
+    rng = np.random.default_rng(N * 31 + Bk)
+    base = rng.standard_normal((1, H, N, d)).astype(np.float32)
+    q = workloads.round_to_bf16(base + 0.5 * rng.standard_normal((1, H, N, d)).astype(np.float32))
+    k = workloads.round_to_bf16(base + 0.5 * rng.standard_normal((1, H, N, d)).astype(np.float32))
+    v = workloads.round_to_bf16(rng.standard_normal((1, H, N, d)).astype(np.float32))
+    run = Run(w, inputs=(q, k, v), seed=5)
+    blocks = run.blocks(64)
+    check_kmeans(run, blocks)
+    check_scores(run, blocks)
+    check_sampler(run, blocks)
+    check_sampler_any_size(run)
+    check_attention(run, blocks)
+    if density == 1.0:
+        for h in range(H):
+            o, lse = dense_attention(q[0, h], k[0, h], v[0, h], run.scale)
+            err = np.abs(run.out[0, h] - o)
+            assert err.max() <= 2e-2
+            assert np.linalg.norm(run.out[0, h] - o) / np.linalg.norm(o) <= 1e-2
+
+
+def test_empty_rows_give_zero_output():
+    run = _run("tiny", density=0.25)
+    cnt = run.cnt_d.clone()
+    cnt[0, 0, 1] = 0
+    cnt[0, 0, 3] = 0
+    out, lse = ab.ab_attn_fwd(run.desc, run.qd, run.kd, run.vd, run.idx_d, run.wts_d, cnt)
+    torch.cuda.synchronize()
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    assert np.all(out[0, 0, 64:128] == 0) and np.all(np.isneginf(lse[0, 0, 64:128]))
+    assert np.all(out[0, 0, 192:256] == 0) and np.all(np.isneginf(lse[0, 0, 192:256]))
+    np.testing.assert_array_equal(out[0, 0, :64], run.out[0, 0, :64])
+
+
+def test_injected_index_lists_bf16():
+    """Attention on hand-made lists: unsorted-free ascending lists with the ragged tail block and weights != 1."""
+    _gpu()
+    N, H, d, Bq, Bk = 1000, 1, 128, 128, 32
+    rng = np.random.default_rng(4)
+    q = workloads.round_to_bf16(rng.standard_normal((1, H, N, d)).astype(np.float32))
+    k = workloads.round_to_bf16(rng.standard_normal((1, H, N, d)).astype(np.float32))
+    v = workloads.round_to_bf16(rng.standard_normal((1, H, N, d)).astype(np.float32))
+    desc = ab.Desc(1, H, N, d, ab.AB_BF16, Bq, Bk, 8)
+    nqb, nkb = desc.nqb, desc.nkb
+    idx = np.zeros((1, H, nqb, nkb), np.int32)
+    wts = np.zeros((1, H, nqb, nkb), np.float32)
+    cnt = np.zeros((1, H, nqb), np.int32)
+    for i in range(nqb):
+        c = [1, 3, 5, 2, nkb][i % 5]
+        sel = np.sort(rng.choice(nkb, size=c, replace=False))
+        if i % 2 == 0:
+            sel = np.unique(np.append(sel[:-1], nkb - 1)) if c > 1 else np.array([nkb - 1])
+        idx[0, 0, i, :sel.size] = sel
+        wts[0, 0, i, :sel.size] = rng.uniform(1.0, 50.0, size=sel.size).astype(np.float32)
+        cnt[0, 0, i] = sel.size
+    dev = lambda x, dt=None: (torch.from_numpy(x).to(dt) if dt else torch.from_numpy(x)).to("cuda:0")
+    out, lse = ab.ab_attn_fwd(desc, dev(q, torch.bfloat16), dev(k, torch.bfloat16), dev(v, torch.bfloat16), dev(idx),
+                              dev(wts), dev(cnt))
+    torch.cuda.synchronize()
+    out = out.float().cpu().numpy()
+    lse = lse.cpu().numpy()
+    for i in range(nqb):
+        lo, hi = i * Bq, min(N, (i + 1) * Bq)
+        c = cnt[0, 0, i]
+        o_ref, l_ref = sparse_ht_attention(q[0, 0, lo:hi], k[0, 0], v[0, 0], idx[0, 0, i, :c], wts[0, 0, i, :c], Bk,
+                                           1 / math.sqrt(d))
+        assert np.abs(out[0, 0, lo:hi] - o_ref).max() <= 2e-2
+        assert np.abs(lse[0, 0, lo:hi] - l_ref).max() <= 1e-3 * max(1.0, np.abs(l_ref).max())
