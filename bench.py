@@ -1,0 +1,256 @@
+"""Benchmark: one layer of AB-Attention's block-sparse attention on one MI355X.
+
+A step is the whole path on one batch of synthetic video-shaped input already
+resident in HBM: ab_score (IBCS k-means + block estimates), ab_sample (SIP) and
+ab_attn_fwd (weighted gather attention), enqueued on one stream.
+
+Prints one JSON line. `value` is the dense-equivalent attention throughput,
+4*B*H*N^2*d / (time of one whole step), in TFLOP/s; `ms_per_step` is ms per
+layer. `roofline` describes the attention kernel: its actually computed FLOPs
+(4*d*sum over query rows of the kept keys) per launch divided by its average
+launch time measured with HIP events on the stream it runs on, against the
+dense bf16 matrix-core peak. `cpu_baseline` times the CPU oracle on a bounded
+sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak (published)
+METRIC = "dense-equivalent attention TFLOP/s and ms/layer at ~10% density, 1 MI355X"
+ATTN_SOURCE = os.path.join(ROOT, "block_sparse_attention_ibcs_amd", "csrc", "attn_fwd.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_wan1.3b_traffic.txt")
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="wan1.3b", help="wan1.3b (default), wan14b or hunyuan")
+    ap.add_argument("--density", type=float, default=None)
+    ap.add_argument("--k-block", type=int, default=None)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="wall time budget of the CPU oracle sample")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run one device copy of this many MiB before timing (reference kernel for HBM counters)")
+    return ap.parse_args()
+
+
+def attn_source_digest():
+    with open(ATTN_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic(workload):
+    """HBM bytes per attention launch from the committed counter summary, if it matches the current kernel."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != attn_source_digest() or vals.get("workload") != workload:
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, q, k, v, density, seed, budget_s):
+    """Time the oracle (IBCS + SIP + weighted attention) on query blocks of head 0 for about budget_s seconds."""
+    import numpy as np
+
+    import oracle
+
+    threads = os.cpu_count() or 1
+    try:
+        from threadpoolctl import threadpool_info
+
+        info = threadpool_info()
+        if info:
+            threads = max(int(t.get("num_threads", 1)) for t in info)
+    except Exception:
+        pass
+    p = oracle.Params(w.q_block, w.k_block, w.n_clusters, w.kmeans_iters, density, bf16=w.dtype == "bf16")
+    # a spread of query blocks of head 0
+    order = np.random.default_rng(1).permutation(w.nqb)
+    t0 = time.perf_counter()
+    done = []
+    for i in order:
+        oracle.run_blocks(q, k, v, p, seed, [(0, 0, int(i))])
+        done.append(int(i))
+        if time.perf_counter() - t0 >= budget_s and len(done) >= 2:
+            break
+    dt = time.perf_counter() - t0
+    rows = sum(min(w.q_block, w.N - i * w.q_block) for i in done)
+    dense_flops = 4.0 * rows * w.N * w.d
+    return {
+        "value": dense_flops / dt / 1e12,
+        "unit": "TFLOP/s (dense-equivalent)",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{len(done)} query blocks ({rows} query rows) of head 0 through IBCS k-means, block scores, "
+                  f"SIP draw and weighted attention in float64/numpy; {dt:.1f} s wall "
+                  f"({dt / len(done) * w.H * w.nqb:.0f} s extrapolated per layer)",
+        "ms_per_layer_extrapolated": dt / len(done) * w.H * w.nqb * 1e3,
+    }
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path is single-GPU by design "
+              "(heads shard across GPUs with no exchange, see DESIGN.md).", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import block_sparse_attention_ibcs_amd as ab
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    ab.load_library()  # fails loudly if the HIP library is not built
+    w = workloads.get(args.workload)
+    if args.k_block:
+        w = w.with_(k_block=args.k_block)
+    density = w.density if args.density is None else args.density
+    q, k, v = workloads.generate(w, seed=0)
+    dev = torch.device("cuda:0")
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    qd, kd, vd = (torch.from_numpy(x).to(tdt).to(dev) for x in (q, k, v))
+    desc = ab.Desc.for_tensor(qd, w.q_block, w.k_block, w.n_clusters, w.kmeans_iters)
+    nqb, nkb = desc.nqb, desc.nkb
+    rows = (w.B, w.H, nqb)
+    ws = ab.alloc_workspace(desc, dev)
+    scores = torch.empty(rows + (nkb,), dtype=torch.float32, device=dev)
+    idx = torch.empty(rows + (nkb,), dtype=torch.int32, device=dev)
+    wts = torch.empty(rows + (nkb,), dtype=torch.float32, device=dev)
+    cnt = torch.empty(rows, dtype=torch.int32, device=dev)
+    out = torch.empty_like(qd)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+
+    if args.copy_calibration_mib > 0:
+        nbytes = args.copy_calibration_mib << 20
+        src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    stream = torch.cuda.current_stream()
+    ev = {name: [] for name in ("score", "sample", "attn")}
+
+    def step(record=False):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if record else None
+        if record:
+            e[0].record(stream)
+        ab.ab_score(desc, qd, kd, scores=scores, workspace=ws)
+        if record:
+            e[1].record(stream)
+        ab.ab_sample(desc, scores, density, args.seed, idx=idx, weights=wts, counts=cnt, want_mask=False)
+        if record:
+            e[2].record(stream)
+        ab.ab_attn_fwd(desc, qd, kd, vd, idx, wts, cnt, out=out, lse=lse)
+        if record:
+            e[3].record(stream)
+            ev["score"].append((e[0], e[1]))
+            ev["sample"].append((e[1], e[2]))
+            ev["attn"].append((e[2], e[3]))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall / args.steps * 1e3
+    # per-stage durations with HIP events on the launch stream (separate pass so the headline
+    # number carries no event overhead)
+    for _ in range(args.steps):
+        step(record=True)
+    torch.cuda.synchronize()
+    stage_ms = {k_: float(np.mean([a.elapsed_time(b) for a, b in v_])) for k_, v_ in ev.items()}
+
+    # actually computed attention work of one launch: 4*d*sum over query rows of the kept keys
+    tail = w.N - (nkb - 1) * w.k_block
+    counts = cnt.to(torch.int64)
+    last_kept = torch.zeros_like(counts)
+    nz = counts > 0
+    last_idx = torch.gather(idx.to(torch.int64), 3, (counts.clamp(min=1) - 1).unsqueeze(-1)).squeeze(-1)
+    last_kept[nz & (last_idx == nkb - 1)] = 1
+    keys = counts * w.k_block - last_kept * (w.k_block - tail)
+    rows_per_block = torch.full((nqb,), w.q_block, dtype=torch.int64, device=dev)
+    rows_per_block[-1] = w.N - (nqb - 1) * w.q_block
+    actual_flops = float((4 * w.d * (keys * rows_per_block.view(1, 1, -1)).sum()).item())
+    dense = w.dense_flops()
+    realised = float(counts.sum().item()) / (w.B * w.H * nqb * nkb)
+
+    attn_s = stage_ms["attn"] / 1e3
+    achieved = actual_flops / attn_s / 1e12
+    traffic = read_traffic(args.workload)
+    result = {
+        "metric": METRIC,
+        "value": dense / (ms_per_step / 1e3) / 1e12,
+        "unit": "TFLOP/s (dense-equivalent)",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded smooth 3D positional field + noise; no model weights)",
+        "config": {
+            "workload": f"{args.workload}: B={w.B} H={w.H} grid={'x'.join(map(str, w.grid))} N={w.N} d={w.d} "
+                        f"Bq={w.q_block} Bk={w.k_block} C={w.n_clusters} T={w.kmeans_iters} density={density}",
+            "seq_len": w.N,
+            "heads": w.H,
+            "density": density,
+            "realised_density": realised,
+            "stage_ms": stage_ms,
+            "attn_actual_tflops": achieved,
+            "attn_dense_equivalent_tflops": dense / attn_s / 1e12,
+            "layer_actual_tflops_excl_scorer": actual_flops / (ms_per_step / 1e3) / 1e12,
+        },
+        "roofline": {
+            "kernel": "attn_fwd_bf16",
+            "bound": "mfma",
+            "achieved": achieved,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": achieved / PEAK_BF16_TFLOPS,
+            "traffic": traffic,
+            "flops_per_launch": actual_flops,
+            "launch_ms": stage_ms["attn"],
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, q, k, v, density, args.seed, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
