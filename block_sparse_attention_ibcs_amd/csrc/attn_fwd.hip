@@ -32,35 +32,47 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kSlots = 64;
 
-template <int D>
+template <int D, int BQ>
 struct AttnCfg {
-  static constexpr int kKPitch = D * 2 + 16;      // bytes per key row of the K tile
-  static constexpr int kVPitch = kSlots * 2 + 8;  // bytes per dim row of the transposed V tile
-  static constexpr int kKBytes = kSlots * kKPitch;
-  static constexpr int kVBytes = D * kVPitch;
-  static constexpr int kChunks = D / 8;           // 16-byte chunks per key row
+  static constexpr int kThreads = BQ * 2;          // one wave per 32 query rows
+  static constexpr int kPitch = D * 2 + 16;        // bytes per slot row of a K or V tile (padded)
+  static constexpr int kTileBytes = kSlots * kPitch;
+  static constexpr int kChunks = D / 8;            // 16-byte chunks per key row
+  static constexpr int kPerThread = kSlots * kChunks / kThreads;  // chunks of one matrix per thread
+  static constexpr int kWindow = 512;              // kept-list entries staged in LDS at a time
+};
+
+// LDS: two K tiles, two V tiles (natural [slot][d] layout), per-slot log-weights
+// of both tiles, and a window of the kept-block list (first key, log2 weight).
+template <int D, int BQ>
+struct AttnSmem {
+  using Cfg = AttnCfg<D, BQ>;
+  unsigned char k[2][Cfg::kTileBytes];
+  unsigned char v[2][Cfg::kTileBytes];
+  float lw[2][kSlots];
+  int ent_key[Cfg::kWindow];
+  float ent_lw[Cfg::kWindow];
 };
 
 template <int D, int BQ>
-__global__ __launch_bounds__(BQ * 2) void attn_fwd_bf16(Dims P, const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(BQ * 2) __attribute__((amdgpu_waves_per_eu(BQ == 128 ? 2 : 1, 2))) void attn_fwd_bf16(Dims P, const uint16_t* __restrict__ q,
                                                          const uint16_t* __restrict__ k,
                                                          const uint16_t* __restrict__ v,
                                                          const int32_t* __restrict__ idx,
                                                          const float* __restrict__ weights,
                                                          const int32_t* __restrict__ counts,
                                                          uint16_t* __restrict__ out, float* __restrict__ lse) {
-  using Cfg = AttnCfg<D>;
-  constexpr int NT = BQ * 2;
-  __shared__ __align__(16) unsigned char Ks[Cfg::kKBytes];
-  __shared__ __align__(16) unsigned char Vt[Cfg::kVBytes];
-  __shared__ int slot_key[kSlots];
-  __shared__ float slot_lw[kSlots];
+  using Cfg = AttnCfg<D, BQ>;
+  constexpr int NT = Cfg::kThreads;
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  AttnSmem<D, BQ>& sm = *reinterpret_cast<AttnSmem<D, BQ>*>(smem_raw);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, col = lane & 31;
   const int blk = blockIdx.x;  // (b*H + h)*nqb + i
   const int i = blk % P.nqb, bh = blk / P.nqb;
   const int N = P.N, Bk = P.Bk;
+  const int bk_shift = __builtin_ctz(Bk);
   const int row0 = i * BQ;
   const int n = min(BQ, N - row0);
   const int cnt = counts[blk];
@@ -73,11 +85,11 @@ __global__ __launch_bounds__(BQ * 2) void attn_fwd_bf16(Dims P, const uint16_t* 
   const int qr = wave * 32 + col;
   bf16x8_t qf[D / 16];
   {
-    const uint16_t* src = q + (size_t(bh) * N + row0 + qr) * D + half * 8;
+    const uint16_t* src = q + (size_t(bh) * N + row0 + min(qr, n - 1)) * D + half * 8;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
-      uint4 u = make_uint4(0, 0, 0, 0);
-      if (qr < n) u = *reinterpret_cast<const uint4*>(src + kk * 16);
+      uint4 u = *reinterpret_cast<const uint4*>(src + kk * 16);
+      if (qr >= n) u = make_uint4(0, 0, 0, 0);
       qf[kk] = as_bf16x8(u);
     }
   }
@@ -87,99 +99,158 @@ __global__ __launch_bounds__(BQ * 2) void attn_fwd_bf16(Dims P, const uint16_t* 
   float m = -__builtin_inff(), l = 0.0f;
   const float c2 = P.scale * kLog2e;
 
-  const int ntiles = ceil_div(cnt * Bk, kSlots);
-  for (int t = 0; t < ntiles; ++t) {
-    __syncthreads();  // previous tile fully consumed
-    if (tid < kSlots) {
-      const int gs = t * kSlots + tid;
-      const int ord = gs / Bk, e = gs - ord * Bk;
-      int key = -1;
+  const int total = cnt << bk_shift;  // key slots, padding of the ragged tail block included
+  const int ntiles = ceil_div(total, kSlots);
+  int ebase = 0;  // first list entry held in the LDS window
+
+  auto stage_window = [&](int first) {
+    for (int e = tid; e < Cfg::kWindow; e += NT) {
+      const int ord = first + e;
+      int key0 = 0x7FFFFFFF;
       float lw = -__builtin_inff();
       if (ord < cnt) {
-        const int kk = list[ord] * Bk + e;
-        if (kk < N) {
-          key = kk;
-          lw = __builtin_amdgcn_logf(wl[ord]);
-        }
+        key0 = list[ord] << bk_shift;
+        lw = __builtin_amdgcn_logf(wl[ord]);
       }
-      slot_key[tid] = key;
-      slot_lw[tid] = lw;
+      sm.ent_key[e] = key0;
+      sm.ent_lw[e] = lw;
     }
-    __syncthreads();
-    // gather K rows (coalesced 16-byte chunks of each key row)
-    for (int p = tid; p < kSlots * Cfg::kChunks; p += NT) {
-      const int s = p / Cfg::kChunks, ch = p - s * Cfg::kChunks;
-      const int key = slot_key[s];
-      uint4 u = make_uint4(0, 0, 0, 0);
-      if (key >= 0) u = *reinterpret_cast<const uint4*>(kh + size_t(key) * D + ch * 8);
-      *reinterpret_cast<uint4*>(Ks + s * Cfg::kKPitch + ch * 16) = u;
-    }
-    // gather V rows in slot pairs and store them transposed: Vt[dim][slot]
-    for (int p = tid; p < (kSlots / 2) * Cfg::kChunks; p += NT) {
-      const int pr = p / Cfg::kChunks, ch = p - pr * Cfg::kChunks;
-      const int k0 = slot_key[2 * pr], k1 = slot_key[2 * pr + 1];
-      uint4 a = make_uint4(0, 0, 0, 0), b = make_uint4(0, 0, 0, 0);
-      if (k0 >= 0) a = *reinterpret_cast<const uint4*>(vh + size_t(k0) * D + ch * 8);
-      if (k1 >= 0) b = *reinterpret_cast<const uint4*>(vh + size_t(k1) * D + ch * 8);
-      const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t lo = (aw[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
-        const uint32_t hi = (bw[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
-        *reinterpret_cast<uint32_t*>(Vt + (ch * 8 + e) * Cfg::kVPitch + pr * 4) = lo | (hi << 16);
-      }
-    }
-    __syncthreads();
+  };
 
+  // register staging of one tile: kPerThread K chunks and as many V chunks
+  uint4 sk[Cfg::kPerThread], sv[Cfg::kPerThread];
+  float slw = -__builtin_inff();
+  auto load_tile = [&](int t) {
+#pragma unroll
+    for (int r = 0; r < Cfg::kPerThread; ++r) {
+      const int p = tid + r * NT;
+      const int s = p / Cfg::kChunks, ch = p - s * Cfg::kChunks;
+      const int gs = t * kSlots + s;
+      const int ord = gs >> bk_shift;
+      const int key = (ord < cnt) ? sm.ent_key[ord - ebase] + (gs & (Bk - 1)) : N;
+      sk[r] = make_uint4(0, 0, 0, 0);
+      sv[r] = make_uint4(0, 0, 0, 0);
+      if (key < N) {
+        sk[r] = *reinterpret_cast<const uint4*>(kh + size_t(key) * D + ch * 8);
+        sv[r] = *reinterpret_cast<const uint4*>(vh + size_t(key) * D + ch * 8);
+      }
+    }
+    if (tid < kSlots) {
+      const int gs = t * kSlots + tid;
+      const int ord = gs >> bk_shift;
+      slw = -__builtin_inff();
+      if (ord < cnt && sm.ent_key[ord - ebase] + (gs & (Bk - 1)) < N) slw = sm.ent_lw[ord - ebase];
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int r = 0; r < Cfg::kPerThread; ++r) {
+      const int p = tid + r * NT;
+      const int s = p / Cfg::kChunks, ch = p - s * Cfg::kChunks;
+      *reinterpret_cast<uint4*>(sm.k[buf] + s * Cfg::kPitch + ch * 16) = sk[r];
+      *reinterpret_cast<uint4*>(sm.v[buf] + s * Cfg::kPitch + ch * 16) = sv[r];
+    }
+    if (tid < kSlots) sm.lw[buf][tid] = slw;
+  };
+  // the kept-list window must cover every entry tile t touches
+  auto ensure_window = [&](int t) {
+    const int last_ord = min(cnt - 1, ((t + 1) * kSlots - 1) >> bk_shift);
+    if (last_ord >= ebase + Cfg::kWindow) {
+      ebase = (t * kSlots) >> bk_shift;
+      __syncthreads();  // nobody reads the old window any more
+      stage_window(ebase);
+      __syncthreads();
+    }
+  };
+
+  // per-lane constants of the transposed V read: lane J of 16-lane group G points at
+  // slot (J%16)/4 of its group's 4-slot run and dims 4*((J%16)%4) of its 16-dim half
+  const int tgrp = lane >> 4, tj = lane & 15;
+  const int tr_slot = ((tgrp >> 1) << 2) + (tj >> 2);
+  const int tr_dim = ((tgrp & 1) << 4) + ((tj & 3) << 2);
+
+  if (ntiles > 0) {
+    stage_window(0);
+    __syncthreads();
+    load_tile(0);
+    store_tile(0);
+    __syncthreads();
+  }
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1;
+    const bool more = t + 1 < ntiles;
+    if (more) {
+      ensure_window(t + 1);
+      load_tile(t + 1);  // global loads in flight during this tile's math
+    }
+    const unsigned char* kt = sm.k[buf];
+    const unsigned char* vt = sm.v[buf];
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
-      if (t * kSlots + hb * 32 >= cnt * Bk) break;
+      if (t * kSlots + hb * 32 >= total) break;
       f32x16_t acc = {};
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
-        const uint4 a = *reinterpret_cast<const uint4*>(Ks + (hb * 32 + col) * Cfg::kKPitch + (kk * 16 + half * 8) * 2);
+        const uint4 a = *reinterpret_cast<const uint4*>(kt + (hb * 32 + col) * Cfg::kPitch + (kk * 16 + half * 8) * 2);
         acc = mfma32x32x16(as_bf16x8(a), qf[kk], acc);
       }
-      float x[16];
-      float mx = -__builtin_inff();
+      // per-slot log2 weights of this lane's 16 keys (4 runs of 4 consecutive slots)
+      float lw[16];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int s = hb * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
-        x[e] = __builtin_fmaf(acc[e], c2, slot_lw[s]);
-        mx = fmaxf(mx, x[e]);
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const float4 w4 = *reinterpret_cast<const float4*>(&sm.lw[buf][hb * 32 + g4 * 8 + half * 4]);
+        lw[4 * g4 + 0] = w4.x;
+        lw[4 * g4 + 1] = w4.y;
+        lw[4 * g4 + 2] = w4.z;
+        lw[4 * g4 + 3] = w4.w;
       }
-      mx = fmaxf(mx, swap_halves(mx));
-      // a window of only padding slots after real keys leaves mn = m (finite)
-      const float mn = fmaxf(m, mx);
-      const float alpha = fast_exp2(m - mn);
-      float ps = 0.0f;
+      // probabilities against the running row max; the max is only moved (and O
+      // rescaled) when some probability of this block would exceed 2^8
       float p[16];
+      float ps = 0.0f;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        p[e] = fast_exp2(x[e] - mn);
+        p[e] = fast_exp2(__builtin_fmaf(acc[e], c2, lw[e] - m));
         ps += p[e];
       }
-      ps += swap_halves(ps);
-      l = l * alpha + ps;
-      m = mn;
+      ps = pair_sum(ps);
+      if (__builtin_amdgcn_ballot_w64(!(ps <= 256.0f)) != 0) {
+        float mx = -__builtin_inff();
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, __builtin_fmaf(acc[e], c2, lw[e]));
+        mx = pair_max(mx);
+        const float mn = fmaxf(m, mx);
+        const float alpha = fast_exp2(m - mn);  // 0 on the first block (m = -inf)
+        l *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+        m = mn;
+        ps = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          p[e] = fast_exp2(__builtin_fmaf(acc[e], c2, lw[e] - m));
+          ps += p[e];
+        }
+        ps = pair_sum(ps);
+      }
+      l += ps;
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
         bf16x8_t pb;
 #pragma unroll
         for (int e = 0; e < 8; ++e) pb[e] = __bf16(p[8 * g + e]);
-        const int s0 = hb * 32 + 16 * g + half * 4;
+        const int s0 = hb * 32 + 16 * g + tr_slot;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-          const unsigned char* vr = Vt + (db * 32 + col) * Cfg::kVPitch;
-          const uint2 lo = *reinterpret_cast<const uint2*>(vr + s0 * 2);
-          const uint2 hi = *reinterpret_cast<const uint2*>(vr + (s0 + 8) * 2);
-          const uint4 av = make_uint4(lo.x, lo.y, hi.x, hi.y);
-          o[db] = mfma32x32x16(as_bf16x8(av), pb, o[db]);
+          const unsigned char* base = vt + s0 * Cfg::kPitch + (db * 32 + tr_dim) * 2;
+          const uint2 lo = lds_read_tr16(base);
+          const uint2 hi = lds_read_tr16(base + 8 * Cfg::kPitch);
+          o[db] = mfma32x32x16(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), pb, o[db]);
         }
       }
     }
+    if (more) store_tile(buf ^ 1);
+    __syncthreads();
   }
 
   // epilogue: O^T lane layout -> row qr, dims db*32 + (e/4)*8 + half*4 + e%4
@@ -279,34 +350,39 @@ __global__ __launch_bounds__(128) void attn_fwd_f32(Dims P, const float* __restr
   }
 }
 
+template <int D, int BQ>
+hipError_t launch_bf16(const Dims& P, const void* q, const void* k, const void* v, const int32_t* idx,
+                       const float* weights, const int32_t* counts, void* out, float* lse, hipStream_t s) {
+  auto kern = attn_fwd_bf16<D, BQ>;
+  const size_t lds = sizeof(AttnSmem<D, BQ>);
+  static const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                  hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(P.B * P.H * P.nqb), dim3(AttnCfg<D, BQ>::kThreads), lds, s, P,
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+                     idx, weights, counts, static_cast<uint16_t*>(out), lse);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_attn_fwd(const Dims& P, const void* q, const void* k, const void* v, const int32_t* idx,
                            const float* weights, const int32_t* counts, void* out, float* lse, hipStream_t s) {
-  const dim3 grid(P.B * P.H * P.nqb);
   if (P.bf16) {
-    auto Q = static_cast<const uint16_t*>(q);
-    auto Kp = static_cast<const uint16_t*>(k);
-    auto Vp = static_cast<const uint16_t*>(v);
-    auto O = static_cast<uint16_t*>(out);
-    if (P.d == 128 && P.Bq == 128)
-      hipLaunchKernelGGL((attn_fwd_bf16<128, 128>), grid, dim3(256), 0, s, P, Q, Kp, Vp, idx, weights, counts, O, lse);
-    else if (P.d == 128)
-      hipLaunchKernelGGL((attn_fwd_bf16<128, 64>), grid, dim3(128), 0, s, P, Q, Kp, Vp, idx, weights, counts, O, lse);
-    else if (P.Bq == 128)
-      hipLaunchKernelGGL((attn_fwd_bf16<64, 128>), grid, dim3(256), 0, s, P, Q, Kp, Vp, idx, weights, counts, O, lse);
-    else
-      hipLaunchKernelGGL((attn_fwd_bf16<64, 64>), grid, dim3(128), 0, s, P, Q, Kp, Vp, idx, weights, counts, O, lse);
-  } else {
-    auto Q = static_cast<const float*>(q);
-    auto Kp = static_cast<const float*>(k);
-    auto Vp = static_cast<const float*>(v);
-    auto O = static_cast<float*>(out);
-    if (P.d == 128)
-      hipLaunchKernelGGL(attn_fwd_f32<128>, grid, dim3(P.Bq), 0, s, P, Q, Kp, Vp, idx, weights, counts, O, lse);
-    else
-      hipLaunchKernelGGL(attn_fwd_f32<64>, grid, dim3(P.Bq), 0, s, P, Q, Kp, Vp, idx, weights, counts, O, lse);
+    if (P.d == 128 && P.Bq == 128) return launch_bf16<128, 128>(P, q, k, v, idx, weights, counts, out, lse, s);
+    if (P.d == 128) return launch_bf16<128, 64>(P, q, k, v, idx, weights, counts, out, lse, s);
+    if (P.Bq == 128) return launch_bf16<64, 128>(P, q, k, v, idx, weights, counts, out, lse, s);
+    return launch_bf16<64, 64>(P, q, k, v, idx, weights, counts, out, lse, s);
   }
+  const dim3 grid(P.B * P.H * P.nqb);
+  auto Q = static_cast<const float*>(q);
+  auto Kp = static_cast<const float*>(k);
+  auto Vp = static_cast<const float*>(v);
+  auto O = static_cast<float*>(out);
+  if (P.d == 128)
+    hipLaunchKernelGGL(attn_fwd_f32<128>, grid, dim3(P.Bq), 0, s, P, Q, Kp, Vp, idx, weights, counts, O, lse);
+  else
+    hipLaunchKernelGGL(attn_fwd_f32<64>, grid, dim3(P.Bq), 0, s, P, Q, Kp, Vp, idx, weights, counts, O, lse);
   return hipGetLastError();
 }
 

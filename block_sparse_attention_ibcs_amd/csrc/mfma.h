@@ -26,6 +26,30 @@ __device__ __forceinline__ f32x16_t mfma32x32x16(bf16x8_t a, bf16x8_t b, f32x16_
 // Value held by lane l ^ 32 (the other half of the wave).
 __device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
 
+// v_permlane32_swap with the same value in both operands: result[0] holds
+// x[l % 32] and result[1] holds x[l % 32 + 32] in every lane l, so a commutative
+// combine of the two is the pair result of lanes l and l ^ 32 (identical in both).
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element
+// (i % 4) of the 4-element (8-byte) chunks addressed by lanes i/4, i/4 + 4,
+// i/4 + 8 and i/4 + 12 of its group (verified on gfx950).
+__device__ __forceinline__ uint2 lds_read_tr16(const void* lds_ptr) {
+  const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4_t*)((__attribute__((address_space(3))) char*)(lds_ptr)));
+  return __builtin_bit_cast(uint2, v);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
