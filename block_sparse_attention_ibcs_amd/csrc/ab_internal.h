@@ -24,6 +24,19 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 
 __host__ __device__ constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+// MI355X deals consecutive workgroup ids round-robin to its 8 XCDs, each with
+// its own L2. This bijection on [0, n) gives every XCD one contiguous range of
+// logical ids, so neighbouring work items (which read overlapping data) share
+// an L2.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_remap(int pid, int n) {
+  const int xcd = pid % kXcds, local = pid / kXcds;
+  const int per = (n + kXcds - 1) / kXcds;
+  const int tall = n % kXcds;  // XCDs that receive `per` ids; the rest receive per - 1
+  if (tall == 0 || xcd < tall) return xcd * per + local;
+  return tall * per + (xcd - tall) * (per - 1) + local;
+}
+
 // Derived sizes of one problem.
 struct Dims {
   int B, H, N, d, Bq, Bk, C, T;

@@ -34,42 +34,48 @@ constexpr int kSlots = 64;
 
 template <int D, int BQ>
 struct AttnCfg {
-  static constexpr int kThreads = BQ * 2;          // one wave per 32 query rows
-  static constexpr int kPitch = D * 2 + 16;        // bytes per slot row of a K or V tile (padded)
-  static constexpr int kTileBytes = kSlots * kPitch;
-  static constexpr int kChunks = D / 8;            // 16-byte chunks per key row
-  static constexpr int kPerThread = kSlots * kChunks / kThreads;  // chunks of one matrix per thread
-  static constexpr int kWindow = 512;              // kept-list entries staged in LDS at a time
+  static constexpr int kWaves = BQ / 32;           // each wave owns 32 query rows
+  static constexpr int kThreads = kWaves * 64;
+  static constexpr int kRowBytes = D * 2;          // one key row of K or V
+  static constexpr int kChunks = D / 8;            // 16-byte chunks per row
+  static constexpr int kTileBytes = kSlots * kRowBytes;
+  static constexpr int kLoadsPerTile = kTileBytes / 1024;     // 64 lanes x 16 bytes per load
+  static constexpr int kLoadsPerWave = kLoadsPerTile / kWaves;
+  static constexpr int kSlotsPerLoad = 1024 / kRowBytes;      // 4 or 8: within one sub-block
 };
 
-// LDS: two K tiles, two V tiles (natural [slot][d] layout), per-slot log-weights
-// of both tiles, and a window of the kept-block list (first key, log2 weight).
-template <int D, int BQ>
-struct AttnSmem {
-  using Cfg = AttnCfg<D, BQ>;
-  unsigned char k[2][Cfg::kTileBytes];
-  unsigned char v[2][Cfg::kTileBytes];
-  float lw[2][kSlots];
-  int ent_key[Cfg::kWindow];
-  float ent_lw[Cfg::kWindow];
-};
+// Tiles are unpadded [slot][d] rows whose 16-byte chunks are permuted by an XOR
+// of the slot index, which makes both LDS read patterns conflict-free on
+// gfx950 (measured): the K fragment read (32 rows, same chunk) and the
+// transposed V read (4 rows x 64 bytes per half wave).
+template <int D>
+__device__ __forceinline__ int k_swz(int slot) {
+  return D == 128 ? (slot & 15) : ((slot >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int v_swz(int slot) {
+  return D == 128 ? ((slot & 3) << 2) : (((slot >> 1) & 1) << 2);
+}
 
 template <int D, int BQ>
-__global__ __launch_bounds__(BQ * 2) __attribute__((amdgpu_waves_per_eu(BQ == 128 ? 2 : 1, 2))) void attn_fwd_bf16(Dims P, const uint16_t* __restrict__ q,
-                                                         const uint16_t* __restrict__ k,
-                                                         const uint16_t* __restrict__ v,
-                                                         const int32_t* __restrict__ idx,
-                                                         const float* __restrict__ weights,
-                                                         const int32_t* __restrict__ counts,
-                                                         uint16_t* __restrict__ out, float* __restrict__ lse) {
+__global__ __launch_bounds__(BQ * 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_fwd_bf16(Dims P, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                   const uint16_t* __restrict__ v, const int32_t* __restrict__ idx,
+                   const float* __restrict__ weights, const int32_t* __restrict__ counts,
+                   uint16_t* __restrict__ out, float* __restrict__ lse) {
   using Cfg = AttnCfg<D, BQ>;
-  constexpr int NT = Cfg::kThreads;
-  extern __shared__ __align__(16) unsigned char smem_raw[];
-  AttnSmem<D, BQ>& sm = *reinterpret_cast<AttnSmem<D, BQ>*>(smem_raw);
+  constexpr uint32_t kOOB = 0x80000000u;  // beyond every buffer: the hardware returns zeros
+  // Four separate LDS objects (K and V, two stages each): the compiler can then tell
+  // that the gather landing in one stage does not alias the reads of the other, and
+  // keeps its vector-memory waits out of the math.
+  __shared__ __align__(16) unsigned char k0s[Cfg::kTileBytes];
+  __shared__ __align__(16) unsigned char k1s[Cfg::kTileBytes];
+  __shared__ __align__(16) unsigned char v0s[Cfg::kTileBytes];
+  __shared__ __align__(16) unsigned char v1s[Cfg::kTileBytes];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, col = lane & 31;
-  const int blk = blockIdx.x;  // (b*H + h)*nqb + i
+  const int blk = xcd_remap(blockIdx.x, gridDim.x);  // (b*H + h)*nqb + i
   const int i = blk % P.nqb, bh = blk / P.nqb;
   const int N = P.N, Bk = P.Bk;
   const int bk_shift = __builtin_ctz(Bk);
@@ -78,8 +84,11 @@ __global__ __launch_bounds__(BQ * 2) __attribute__((amdgpu_waves_per_eu(BQ == 12
   const int cnt = counts[blk];
   const int32_t* list = idx + size_t(blk) * P.nkb;
   const float* wl = weights + size_t(blk) * P.nkb;
-  const uint16_t* kh = k + size_t(bh) * N * D;
-  const uint16_t* vh = v + size_t(bh) * N * D;
+  const int head_bytes = N * Cfg::kRowBytes;
+  const __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(k + size_t(bh) * N * D), (short)0, head_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(v + size_t(bh) * N * D), (short)0, head_bytes, 0x00020000);
 
   // Q^T as the B operand: lane -> query row (wave*32 + col), 8 dims per k step
   const int qr = wave * 32 + col;
@@ -99,158 +108,179 @@ __global__ __launch_bounds__(BQ * 2) __attribute__((amdgpu_waves_per_eu(BQ == 12
   float m = -__builtin_inff(), l = 0.0f;
   const float c2 = P.scale * kLog2e;
 
-  const int total = cnt << bk_shift;  // key slots, padding of the ragged tail block included
+  // key slots: the kept sub-blocks laid end to end; the ragged tail block (always the
+  // last entry when kept) leaves its padding at the very end, so slot gs holds a real
+  // key iff gs < vend
+  const int total = cnt << bk_shift;
   const int ntiles = ceil_div(total, kSlots);
-  int ebase = 0;  // first list entry held in the LDS window
+  const int tail_pad = (cnt > 0 && list[cnt - 1] == P.nkb - 1) ? (P.nkb << bk_shift) - N : 0;
+  const int vend = total - tail_pad;
 
-  auto stage_window = [&](int first) {
-    for (int e = tid; e < Cfg::kWindow; e += NT) {
-      const int ord = first + e;
-      int key0 = 0x7FFFFFFF;
-      float lw = -__builtin_inff();
-      if (ord < cnt) {
-        key0 = list[ord] << bk_shift;
-        lw = __builtin_amdgcn_logf(wl[ord]);
-      }
-      sm.ent_key[e] = key0;
-      sm.ent_lw[e] = lw;
-    }
-  };
-
-  // register staging of one tile: kPerThread K chunks and as many V chunks
-  uint4 sk[Cfg::kPerThread], sv[Cfg::kPerThread];
-  float slw = -__builtin_inff();
-  auto load_tile = [&](int t) {
+  // Kept-list entries and weights are fetched ahead with unconditional (clamped)
+  // loads whose results are only consumed in a later iteration, so no wait on them
+  // ever sits between a tile's gather and its math.
+  // entries(t): the list entry of each of this wave's loads of tile t; one load covers
+  // kSlotsPerLoad consecutive slots of a single sub-block.
+  // Both go through buffer (vector-memory) loads: a scalar load would share its wait
+  // counter with the LDS reads of the math and stall them.
+  const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc((void*)list, (short)0, P.nkb * 4, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void*)wl, (short)0, P.nkb * 4, 0x00020000);
+  auto entries = [&](int t, int (&kv)[Cfg::kLoadsPerWave]) {
 #pragma unroll
-    for (int r = 0; r < Cfg::kPerThread; ++r) {
-      const int p = tid + r * NT;
-      const int s = p / Cfg::kChunks, ch = p - s * Cfg::kChunks;
-      const int gs = t * kSlots + s;
-      const int ord = gs >> bk_shift;
-      const int key = (ord < cnt) ? sm.ent_key[ord - ebase] + (gs & (Bk - 1)) : N;
-      sk[r] = make_uint4(0, 0, 0, 0);
-      sv[r] = make_uint4(0, 0, 0, 0);
-      if (key < N) {
-        sk[r] = *reinterpret_cast<const uint4*>(kh + size_t(key) * D + ch * 8);
-        sv[r] = *reinterpret_cast<const uint4*>(vh + size_t(key) * D + ch * 8);
-      }
-    }
-    if (tid < kSlots) {
-      const int gs = t * kSlots + tid;
-      const int ord = gs >> bk_shift;
-      slw = -__builtin_inff();
-      if (ord < cnt && sm.ent_key[ord - ebase] + (gs & (Bk - 1)) < N) slw = sm.ent_lw[ord - ebase];
+    for (int j = 0; j < Cfg::kLoadsPerWave; ++j) {
+      const int ord = (t * kSlots + (wave * Cfg::kLoadsPerWave + j) * Cfg::kSlotsPerLoad) >> bk_shift;
+      kv[j] = __builtin_amdgcn_raw_buffer_load_b32(rl, uint32_t(min(ord, cnt - 1)) * 4, 0, 0);
     }
   };
-  auto store_tile = [&](int buf) {
+  // weights(t): slot s of tile t belongs to entry (t*64 + s) >> shift, so a tile
+  // touches at most 64/Bk (<= 4) consecutive entries
+  auto weights4 = [&](int t, float (&wv)[4]) {
 #pragma unroll
-    for (int r = 0; r < Cfg::kPerThread; ++r) {
-      const int p = tid + r * NT;
-      const int s = p / Cfg::kChunks, ch = p - s * Cfg::kChunks;
-      *reinterpret_cast<uint4*>(sm.k[buf] + s * Cfg::kPitch + ch * 16) = sk[r];
-      *reinterpret_cast<uint4*>(sm.v[buf] + s * Cfg::kPitch + ch * 16) = sv[r];
-    }
-    if (tid < kSlots) sm.lw[buf][tid] = slw;
+    for (int j = 0; j < 4; ++j)
+      wv[j] = __builtin_bit_cast(
+          float, __builtin_amdgcn_raw_buffer_load_b32(rw, uint32_t(min(((t * kSlots) >> bk_shift) + j, cnt - 1)) * 4, 0, 0));
   };
-  // the kept-list window must cover every entry tile t touches
-  auto ensure_window = [&](int t) {
-    const int last_ord = min(cnt - 1, ((t + 1) * kSlots - 1) >> bk_shift);
-    if (last_ord >= ebase + Cfg::kWindow) {
-      ebase = (t * kSlots) >> bk_shift;
-      __syncthreads();  // nobody reads the old window any more
-      stage_window(ebase);
-      __syncthreads();
+  // asynchronous gather of tile t straight into LDS buffer `buf` (no VGPR staging)
+  auto issue_tile = [&](int t, unsigned char* kdst, unsigned char* vdst, const int (&kv)[Cfg::kLoadsPerWave]) {
+#pragma unroll
+    for (int j = 0; j < Cfg::kLoadsPerWave; ++j) {
+      const int ld = wave * Cfg::kLoadsPerWave + j;
+      const int gs0 = t * kSlots + ld * Cfg::kSlotsPerLoad;
+      const int ord = gs0 >> bk_shift;
+      const int key0 = (ord < cnt) ? (kv[j] << bk_shift) + (gs0 & (Bk - 1)) : N;
+      const int slot = ld * Cfg::kSlotsPerLoad + lane / Cfg::kChunks;
+      const int key = key0 + lane / Cfg::kChunks;
+      const int pos = lane % Cfg::kChunks;
+      const uint32_t base = (key < N) ? uint32_t(key) * Cfg::kRowBytes : kOOB;
+      buffer_load_lds16(rk, kdst + ld * 1024, base + ((pos ^ k_swz<D>(slot)) << 4));
+      buffer_load_lds16(rv, vdst + ld * 1024, base + ((pos ^ v_swz<D>(slot)) << 4));
+    }
+  };
+  // log2 weight of this lane's keys e in [4g, 4g + 4) of half g / 4 (slots
+  // (g/4)*32 + (g%4)*8 + ...), from the four entry weights of tile t
+  auto tile_lw = [&](int t, const float (&wv)[4], float (&lwg)[8]) {
+    float e4[4];
+    const int ord0 = (t * kSlots) >> bk_shift;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) e4[j] = (ord0 + j < cnt) ? __builtin_amdgcn_logf(wv[j]) : -__builtin_inff();
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      const int jl = ((g >> 2) * 32 + (g & 3) * 8) >> bk_shift;
+      lwg[g] = jl == 0 ? e4[0] : jl == 1 ? e4[1] : jl == 2 ? e4[2] : e4[3];
     }
   };
 
-  // per-lane constants of the transposed V read: lane J of 16-lane group G points at
-  // slot (J%16)/4 of its group's 4-slot run and dims 4*((J%16)%4) of its 16-dim half
+  // LDS byte offsets of this lane's fragment reads (independent of the tile)
+  int koff[D / 16];  // K rows col (+32 for the second half), chunk 2*kk + half
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) koff[kk] = col * Cfg::kRowBytes + (((2 * kk + half) ^ k_swz<D>(col)) << 4);
+  // transposed V read: lane J of 16-lane group G points at slot (J%16)/4 of its group's
+  // 4-slot run and dims 4*((J%16)%4) of its 16-dim half of each 32-dim block
   const int tgrp = lane >> 4, tj = lane & 15;
   const int tr_slot = ((tgrp >> 1) << 2) + (tj >> 2);
-  const int tr_dim = ((tgrp & 1) << 4) + ((tj & 3) << 2);
-
-  if (ntiles > 0) {
-    stage_window(0);
-    __syncthreads();
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
+  int voff[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    const int byte = db * 64 + (tgrp & 1) * 32 + (tj & 3) * 8;  // logical byte within the row
+    voff[db] = tr_slot * Cfg::kRowBytes + ((((byte >> 4) ^ v_swz<D>(tr_slot)) << 4) | (byte & 15));
   }
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    const bool more = t + 1 < ntiles;
-    if (more) {
-      ensure_window(t + 1);
-      load_tile(t + 1);  // global loads in flight during this tile's math
+
+  int kv[Cfg::kLoadsPerWave];
+  float wv[4];
+  if (ntiles > 0) {
+    entries(0, kv);
+    __builtin_amdgcn_s_waitcnt(0);
+    issue_tile(0, k0s, v0s, kv);
+    if (ntiles > 1) entries(1, kv);
+    weights4(0, wv);
+  }
+  // Drain every load issued so far (the Q fragments included) so the compiler's
+  // wait-count analysis does not keep waits on them inside the loop.
+  __builtin_amdgcn_s_waitcnt(0);
+  // One tile: wait for its gather, prefetch the next tile into the other stage, then
+  // S^T = K Q^T, softmax with the inverse-probability weights, O^T += V^T P^T.
+  auto step = [&](int t, const unsigned char* kc, const unsigned char* vc, unsigned char* kn, unsigned char* vn) {
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's gather of tile t has landed in LDS
+    __syncthreads();                // ... and every other wave's; tile t-1 is fully consumed
+    float lwg[8];
+    tile_lw(t, wv, lwg);
+    if (t + 1 < ntiles) issue_tile(t + 1, kn, vn, kv);  // lands while tile t is computed
+    if (t + 2 < ntiles) entries(t + 2, kv);
+    if (t + 1 < ntiles) weights4(t + 1, wv);
+    // S^T for both 32-slot halves, as two independent accumulation chains
+    f32x16_t acc[2];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) acc[hb] = f32x16_t{};
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        const uint4 a = *reinterpret_cast<const uint4*>(kc + hb * 32 * Cfg::kRowBytes + koff[kk]);
+        acc[hb] = mfma32x32x16(as_bf16x8(a), qf[kk], acc[hb]);
+      }
     }
-    const unsigned char* kt = sm.k[buf];
-    const unsigned char* vt = sm.v[buf];
+    // padding slots of the last tile get probability 0
+    const bool ragged = (t + 1) * kSlots > vend;
+    if (ragged) {
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      if (t * kSlots + hb * 32 >= total) break;
-      f32x16_t acc = {};
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        const uint4 a = *reinterpret_cast<const uint4*>(kt + (hb * 32 + col) * Cfg::kPitch + (kk * 16 + half * 8) * 2);
-        acc = mfma32x32x16(as_bf16x8(a), qf[kk], acc);
-      }
-      // per-slot log2 weights of this lane's 16 keys (4 runs of 4 consecutive slots)
-      float lw[16];
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const float4 w4 = *reinterpret_cast<const float4*>(&sm.lw[buf][hb * 32 + g4 * 8 + half * 4]);
-        lw[4 * g4 + 0] = w4.x;
-        lw[4 * g4 + 1] = w4.y;
-        lw[4 * g4 + 2] = w4.z;
-        lw[4 * g4 + 3] = w4.w;
-      }
-      // probabilities against the running row max; the max is only moved (and O
-      // rescaled) when some probability of this block would exceed 2^8
-      float p[16];
-      float ps = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        p[e] = fast_exp2(__builtin_fmaf(acc[e], c2, lw[e] - m));
-        ps += p[e];
-      }
-      ps = pair_sum(ps);
-      if (__builtin_amdgcn_ballot_w64(!(ps <= 256.0f)) != 0) {
-        float mx = -__builtin_inff();
-#pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, __builtin_fmaf(acc[e], c2, lw[e]));
-        mx = pair_max(mx);
-        const float mn = fmaxf(m, mx);
-        const float alpha = fast_exp2(m - mn);  // 0 on the first block (m = -inf)
-        l *= alpha;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
-        m = mn;
-        ps = 0.0f;
+      for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          p[e] = fast_exp2(__builtin_fmaf(acc[e], c2, lw[e] - m));
-          ps += p[e];
+          const int gs = t * kSlots + hb * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
+          if (gs >= vend) acc[hb][e] = -__builtin_inff();
         }
-        ps = pair_sum(ps);
-      }
-      l += ps;
+    }
+    // Upper bound of the tile's weighted logits per row; the running max m is moved
+    // (and O, l rescaled) only when the bound exceeds it by more than 8, so every
+    // probability stays in [0, 2^8].
+    float amax = acc[0][0];
 #pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        bf16x8_t pb;
+    for (int e = 1; e < 16; ++e) amax = fmaxf(amax, acc[0][e]);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pb[e] = __bf16(p[8 * g + e]);
-        const int s0 = hb * 32 + 16 * g + tr_slot;
+    for (int e = 0; e < 16; ++e) amax = fmaxf(amax, acc[1][e]);
+    float lwmax = lwg[0];
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const unsigned char* base = vt + s0 * Cfg::kPitch + (db * 32 + tr_dim) * 2;
-          const uint2 lo = lds_read_tr16(base);
-          const uint2 hi = lds_read_tr16(base + 8 * Cfg::kPitch);
-          o[db] = mfma32x32x16(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), pb, o[db]);
-        }
+    for (int g = 1; g < 8; ++g) lwmax = fmaxf(lwmax, lwg[g]);
+    const float ub = pair_max(__builtin_fmaf(amax, c2, lwmax));  // finite: slot 0 of a tile is a real key
+    if (__builtin_amdgcn_ballot_w64(ub > m + 8.0f) != 0) {
+      const float mn = fmaxf(m, ub);
+      const float alpha = fast_exp2(m - mn);  // 0 on the first tile (m = -inf)
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+      m = mn;
+    }
+    // probabilities (written over the logits) and the row sum
+    float ps = 0.0f;
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      const float bias = lwg[g] - m;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x = fast_exp2(__builtin_fmaf(acc[g >> 2][(g & 3) * 4 + e], c2, bias));
+        acc[g >> 2][(g & 3) * 4 + e] = x;
+        ps += x;
       }
     }
-    if (more) store_tile(buf ^ 1);
-    __syncthreads();
+    l += pair_sum(ps);
+    // O^T += V^T P^T over four 16-slot groups; four independent accumulators
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      bf16x8_t pb;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pb[e] = __bf16(acc[g >> 1][8 * (g & 1) + e]);
+      const unsigned char* vrow = vc + 16 * g * Cfg::kRowBytes;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const uint2 lo = lds_read_tr16(vrow + voff[db]);
+        const uint2 hi = lds_read_tr16(vrow + 8 * Cfg::kRowBytes + voff[db]);
+        o[db] = mfma32x32x16(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), pb, o[db]);
+      }
+    }
+  };
+  for (int t = 0; t < ntiles; t += 2) {
+    step(t, k0s, v0s, k1s, v1s);
+    if (t + 1 < ntiles) step(t + 1, k1s, v1s, k0s, v0s);
   }
 
   // epilogue: O^T lane layout -> row qr, dims db*32 + (e/4)*8 + half*4 + e%4
@@ -353,12 +383,7 @@ __global__ __launch_bounds__(128) void attn_fwd_f32(Dims P, const float* __restr
 template <int D, int BQ>
 hipError_t launch_bf16(const Dims& P, const void* q, const void* k, const void* v, const int32_t* idx,
                        const float* weights, const int32_t* counts, void* out, float* lse, hipStream_t s) {
-  auto kern = attn_fwd_bf16<D, BQ>;
-  const size_t lds = sizeof(AttnSmem<D, BQ>);
-  static const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                                  hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(P.B * P.H * P.nqb), dim3(AttnCfg<D, BQ>::kThreads), lds, s, P,
+  hipLaunchKernelGGL((attn_fwd_bf16<D, BQ>), dim3(P.B * P.H * P.nqb), dim3(AttnCfg<D, BQ>::kThreads), 0, s, P,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
                      idx, weights, counts, static_cast<uint16_t*>(out), lse);
   return hipGetLastError();

@@ -53,4 +53,13 @@ __device__ __forceinline__ uint2 lds_read_tr16(const void* lds_ptr) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
+// Asynchronous 16-byte buffer load straight into LDS: lane L's bytes land at
+// lds_base + 16 * L (lds_base must be wave-uniform); an offset past the buffer's
+// size loads zeros (verified on gfx950).
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, void* lds_base, uint32_t voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void*)((__attribute__((address_space(3))) char*)lds_base), 16, voffset, 0,
+      0, 0);
+}
+
 }  // namespace ab
