@@ -50,7 +50,7 @@ struct AttnCfg {
 // transposed V read (4 rows x 64 bytes per half wave).
 template <int D>
 __device__ __forceinline__ int k_swz(int slot) {
-  return D == 128 ? (slot & 15) : ((slot >> 1) & 7);
+  return kfrag_swz<D>(slot);
 }
 template <int D>
 __device__ __forceinline__ int v_swz(int slot) {

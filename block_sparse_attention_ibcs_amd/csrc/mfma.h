@@ -62,4 +62,12 @@ __device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, void
       0, 0);
 }
 
+// 16-byte chunk permutation of an unpadded [key][d] bf16 tile in LDS that makes the
+// MFMA fragment read (32 consecutive rows, same chunk, 16 bytes per lane)
+// conflict-free on gfx950 (measured).
+template <int D>
+__device__ __forceinline__ int kfrag_swz(int row) {
+  return D == 128 ? (row & 15) : ((row >> 1) & 7);
+}
+
 }  // namespace ab

@@ -27,160 +27,173 @@ constexpr int kTileKeys = 64;  // keys per LDS tile (two 32-key MFMA blocks)
 
 template <int D>
 struct LseCfg {
-  static constexpr int kRowPitch = D * 2 + 16;                 // bytes per key row in LDS (padded)
-  static constexpr int kTileBytes = kTileKeys * kRowPitch;      // one buffer
-  static constexpr int kChunksPerRow = D / 8;                   // 16-byte chunks per key row
-  static constexpr int kChunksPerThread = kTileKeys * kChunksPerRow / 256;
+  static constexpr int kWaves = 4;
+  static constexpr int kRows = kWaves * 64;                 // centroid rows per workgroup (64 per wave)
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kChunks = D / 8;                     // 16-byte chunks per key row
+  static constexpr int kTileBytes = kTileKeys * kRowBytes;
+  static constexpr int kLoadsPerWave = kTileBytes / 1024 / kWaves;
+  static constexpr int kKeysPerLoad = 1024 / kRowBytes;
 };
 
-// Running base-2 log-sum-exp state of one centroid row held by a lane pair.
+// Running base-2 log-sum-exp state of one centroid row (identical in the lane pair
+// l, l ^ 32 that holds it).
 struct LseState {
-  float mref;  // reference (log2 units)
+  float mref;  // reference (log2 units); only raised, and only when a block would overflow
   float tot;   // sum of 2^(x - mref) over every key seen in this split
   float sub;   // same, over the keys of the open sub-block (k_block >= 64)
 };
 
-template <int D>
-__global__ __launch_bounds__(256) void score_lse_bf16(Dims P, int split_keys, int splits,
-                                                      const uint16_t* __restrict__ keys,
-                                                      const uint16_t* __restrict__ cent,
-                                                      float* __restrict__ ell,
-                                                      float* __restrict__ lpart) {
+// One centroid row group's epilogue for one 32-key block: logits x (this lane's 16
+// keys of the block), running state st, first key of the block kb.
+template <int BK>
+__device__ __forceinline__ void lse_block(const f32x16_t& acc, LseState& st, float c2, int kb, int key_end,
+                                          int half, bool row_ok, float* ell_row, int C, int nkb) {
+  float ev[16];
+  float s_own = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    ev[e] = fast_exp2(__builtin_fmaf(acc[e], c2, -st.mref));
+    s_own += ev[e];
+  }
+  float s_pair = pair_sum(s_own);
+  // rebase when the reference is unset (first block) or a sum would pass 2^64
+  if (__builtin_amdgcn_ballot_w64(!(s_pair < 1.8446744e19f)) != 0) {
+    float bm = acc[0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) bm = fmaxf(bm, acc[e]);
+    const float nref = fmaxf(st.mref, pair_max(bm) * c2);
+    const float f = fast_exp2(st.mref - nref);  // 0 when the old reference was unset
+    st.tot *= f;
+    st.sub *= f;
+    st.mref = nref;
+    s_own = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      ev[e] = fast_exp2(__builtin_fmaf(acc[e], c2, -st.mref));
+      s_own += ev[e];
+    }
+    s_pair = pair_sum(s_own);
+  }
+  st.tot += s_pair;
+  if constexpr (BK == 16) {
+    float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s0 += ev[e];
+#pragma unroll
+    for (int e = 8; e < 16; ++e) s1 += ev[e];
+    s0 = pair_sum(s0);
+    s1 = pair_sum(s1);
+    const int j = kb / 16 + half;
+    if (row_ok && j < nkb) ell_row[size_t(j) * C] = st.mref + fast_log2(half ? s1 : s0);
+  } else if constexpr (BK == 32) {
+    if (row_ok && half == 0) ell_row[size_t(kb / 32) * C] = st.mref + fast_log2(s_pair);
+  } else {
+    st.sub += s_pair;
+    if (((kb + 32) % BK == 0) || (kb + 32 >= key_end)) {
+      if (row_ok && half == 0) ell_row[size_t(kb / BK) * C] = st.mref + fast_log2(st.sub);
+      st.sub = 0.0f;
+    }
+  }
+}
+
+// Work item = (b*H + h, key split, row tile of 256 centroid rows), row tile fastest,
+// remapped so an XCD holds consecutive row tiles of one head and split (same keys).
+template <int D, int BK>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 4)))
+void score_lse_bf16(Dims P, int split_keys, int splits, int row_tiles, const uint16_t* __restrict__ keys,
+                    const uint16_t* __restrict__ cent, float* __restrict__ ell, float* __restrict__ lpart) {
   using Cfg = LseCfg<D>;
-  extern __shared__ __align__(16) unsigned char smem[];
+  constexpr uint32_t kOOB = 0x80000000u;
+  __shared__ __align__(16) unsigned char kb0[Cfg::kTileBytes];
+  __shared__ __align__(16) unsigned char kb1[Cfg::kTileBytes];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, col = lane & 31;
-  const int bh = blockIdx.z;
-  const int split = blockIdx.y;
-  const int cr = blockIdx.x * 128 + wave * 32 + col;  // centroid row of this lane
-  const bool row_ok = cr < P.mrows;
+  const int wid = xcd_remap(blockIdx.x, gridDim.x);
+  const int rt = wid % row_tiles;
+  const int split = (wid / row_tiles) % splits;
+  const int bh = wid / (row_tiles * splits);
   const int N = P.N;
   const int key_begin = split * split_keys;
   const int key_end = min(N, key_begin + split_keys);
+  const int ntiles = ceil_div(key_end - key_begin, kTileKeys);
+  const float c2 = P.scale * kLog2e;
 
-  // B operand: this lane's centroid, 8 dims per 16-wide k step.
-  bf16x8_t bfrag[D / 16];
-  {
-    const uint16_t* src = cent + (size_t(bh) * P.mrows + cr) * D + half * 8;
+  // B operands: this lane's two centroid rows (row groups), 8 dims per 16-wide k step
+  int cr[2];
+  bool row_ok[2];
+  float* ell_row[2];
+  bf16x8_t bfrag[2][D / 16];
+#pragma unroll
+  for (int rg = 0; rg < 2; ++rg) {
+    cr[rg] = rt * Cfg::kRows + wave * 64 + rg * 32 + col;
+    row_ok[rg] = cr[rg] < P.mrows;
+    const int r = min(cr[rg], P.mrows - 1);
+    const uint16_t* src = cent + (size_t(bh) * P.mrows + r) * D + half * 8;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
-      uint4 u = make_uint4(0, 0, 0, 0);
-      if (row_ok) u = *reinterpret_cast<const uint4*>(src + kk * 16);
-      bfrag[kk] = as_bf16x8(u);
+      uint4 u = *reinterpret_cast<const uint4*>(src + kk * 16);
+      if (!row_ok[rg]) u = make_uint4(0, 0, 0, 0);
+      bfrag[rg][kk] = as_bf16x8(u);
     }
+    ell_row[rg] = ell + (size_t(bh) * P.nqb + r / P.C) * size_t(P.nkb) * P.C + (r % P.C);
   }
-  const size_t ell_row = row_ok ? (size_t(bh) * P.nqb + cr / P.C) * size_t(P.nkb) * P.C + (cr % P.C) : 0;
-  const float c2 = P.scale * kLog2e;
-  const int Bk = P.Bk;
-
-  const uint16_t* kbase = keys + size_t(bh) * N * D;
-  const int ntiles = ceil_div(key_end - key_begin, kTileKeys);
-
-  // cooperative tile load: thread -> (row, chunk)
-  uint4 stage[Cfg::kChunksPerThread];
-  auto load_tile = [&](int t) {
-    const int k0 = key_begin + t * kTileKeys;
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(keys + size_t(bh) * N * D), (short)0, N * Cfg::kRowBytes, 0x00020000);
+  auto issue_tile = [&](int t, unsigned char* dst) {
 #pragma unroll
-    for (int r = 0; r < Cfg::kChunksPerThread; ++r) {
-      const int p = tid + r * 256;
-      const int row = p / Cfg::kChunksPerRow, ch = p % Cfg::kChunksPerRow;
-      const int key = k0 + row;
-      stage[r] = make_uint4(0, 0, 0, 0);
-      if (key < key_end) stage[r] = *reinterpret_cast<const uint4*>(kbase + size_t(key) * D + ch * 8);
+    for (int j = 0; j < Cfg::kLoadsPerWave; ++j) {
+      const int ld = wave * Cfg::kLoadsPerWave + j;
+      const int krow = ld * Cfg::kKeysPerLoad + lane / Cfg::kChunks;
+      const int key = key_begin + t * kTileKeys + krow;
+      const int pos = lane % Cfg::kChunks;
+      const uint32_t off = key < key_end ? uint32_t(key) * Cfg::kRowBytes + ((pos ^ kfrag_swz<D>(krow)) << 4) : kOOB;
+      buffer_load_lds16(rk, dst + ld * 1024, off);
     }
   };
-  auto store_tile = [&](int buf) {
-    unsigned char* base = smem + buf * Cfg::kTileBytes;
+  int koff[D / 16];
 #pragma unroll
-    for (int r = 0; r < Cfg::kChunksPerThread; ++r) {
-      const int p = tid + r * 256;
-      const int row = p / Cfg::kChunksPerRow, ch = p % Cfg::kChunksPerRow;
-      *reinterpret_cast<uint4*>(base + row * Cfg::kRowPitch + ch * 16) = stage[r];
-    }
-  };
+  for (int kk = 0; kk < D / 16; ++kk) koff[kk] = col * Cfg::kRowBytes + (((2 * kk + half) ^ kfrag_swz<D>(col)) << 4);
 
-  LseState st{-__builtin_inff(), 0.0f, 0.0f};
-  if (ntiles > 0) load_tile(0);
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    store_tile(buf);
-    __syncthreads();
-    if (t + 1 < ntiles) load_tile(t + 1);
-    const unsigned char* kt = smem + buf * Cfg::kTileBytes;
+  LseState st[2] = {{-__builtin_inff(), 0.0f, 0.0f}, {-__builtin_inff(), 0.0f, 0.0f}};
+  if (ntiles > 0) issue_tile(0, kb0);
+  __builtin_amdgcn_s_waitcnt(0);
+  auto step = [&](int t, const unsigned char* kc, unsigned char* kn) {
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's part of tile t is in LDS
+    __syncthreads();                // all of it; tile t-1 is consumed
+    if (t + 1 < ntiles) issue_tile(t + 1, kn);
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      const int kb = key_begin + t * kTileKeys + blk * 32;  // first key of this 32-key block
+    for (int hb = 0; hb < 2; ++hb) {
+      const int kb = key_begin + t * kTileKeys + hb * 32;  // first key of this 32-key block (uniform)
       if (kb >= key_end) break;
-      f32x16_t acc = {};
+      f32x16_t acc[2] = {f32x16_t{}, f32x16_t{}};
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
-        const uint4 a = *reinterpret_cast<const uint4*>(kt + (blk * 32 + col) * Cfg::kRowPitch + (kk * 16 + half * 8) * 2);
-        acc = mfma32x32x16(as_bf16x8(a), bfrag[kk], acc);
+        const uint4 a = *reinterpret_cast<const uint4*>(kc + hb * 32 * Cfg::kRowBytes + koff[kk]);
+        acc[0] = mfma32x32x16(as_bf16x8(a), bfrag[0][kk], acc[0]);
+        acc[1] = mfma32x32x16(as_bf16x8(a), bfrag[1][kk], acc[1]);
       }
-      float x[16];
-#pragma unroll
-      for (int e = 0; e < 16; ++e) x[e] = acc[e];
-      if (kb + 32 > key_end) {
+      if (kb + 32 > key_end) {  // ragged end of the keys
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int key = kb + (e >> 2) * 8 + half * 4 + (e & 3);
-          if (key >= key_end) x[e] = -__builtin_inff();
+          const bool dead = kb + (e >> 2) * 8 + half * 4 + (e & 3) >= key_end;
+          if (dead) {
+            acc[0][e] = -__builtin_inff();
+            acc[1][e] = -__builtin_inff();
+          }
         }
       }
-      // exponentials against the running reference; rebase when it is unset or would overflow
-      float ev[16];
-      float s_own = 0.0f;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        ev[e] = fast_exp2(__builtin_fmaf(x[e], c2, -st.mref));
-        s_own += ev[e];
-      }
-      float s_pair = s_own + swap_halves(s_own);
-      if (!(s_pair < 1.8446744e19f)) {  // 2^64; also catches the unset reference (inf/NaN)
-        float bm = x[0];
-#pragma unroll
-        for (int e = 1; e < 16; ++e) bm = fmaxf(bm, x[e]);
-        bm = fmaxf(bm, swap_halves(bm));
-        const float nref = bm * c2;
-        const float f = fast_exp2(st.mref - nref);  // 0 when the old reference was unset
-        st.tot *= f;
-        st.sub *= f;
-        st.mref = nref;
-        s_own = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          ev[e] = fast_exp2(__builtin_fmaf(x[e], c2, -st.mref));
-          s_own += ev[e];
-        }
-        s_pair = s_own + swap_halves(s_own);
-      }
-      st.tot += s_pair;
-      if (Bk == 16) {
-        float s0 = 0.0f, s1 = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) s0 += ev[e];
-#pragma unroll
-        for (int e = 8; e < 16; ++e) s1 += ev[e];
-        s0 += swap_halves(s0);
-        s1 += swap_halves(s1);
-        const int j = kb / 16 + half;
-        const float v = st.mref + fast_log2(half ? s1 : s0);
-        if (row_ok && j < P.nkb) ell[ell_row + size_t(j) * P.C] = v;
-      } else if (Bk == 32) {
-        const int j = kb / 32;
-        if (row_ok && half == 0) ell[ell_row + size_t(j) * P.C] = st.mref + fast_log2(s_pair);
-      } else {
-        st.sub += s_pair;
-        const bool last = ((kb + 32) % Bk == 0) || (kb + 32 >= key_end);
-        if (last) {
-          const int j = kb / Bk;
-          if (row_ok && half == 0) ell[ell_row + size_t(j) * P.C] = st.mref + fast_log2(st.sub);
-          st.sub = 0.0f;
-        }
-      }
+      for (int rg = 0; rg < 2; ++rg) lse_block<BK>(acc[rg], st[rg], c2, kb, key_end, half, row_ok[rg], ell_row[rg], P.C, P.nkb);
     }
+  };
+  for (int t = 0; t < ntiles; t += 2) {
+    step(t, kb0, kb1);
+    if (t + 1 < ntiles) step(t + 1, kb1, kb0);
   }
-  if (row_ok && half == 0) lpart[(size_t(bh) * P.mrows + cr) * splits + split] = st.mref + fast_log2(st.tot);
+#pragma unroll
+  for (int rg = 0; rg < 2; ++rg)
+    if (row_ok[rg] && half == 0) lpart[(size_t(bh) * P.mrows + cr[rg]) * splits + split] = st[rg].mref + fast_log2(st[rg].tot);
 }
 
 // fp32 inputs: plain VALU dot products, one thread per (centroid, sub-block).
@@ -270,7 +283,7 @@ ScoreWs score_ws_layout(const Dims& D, int num_cus) {
   // key splits: enough (row tile, split, head) workgroups for two waves of the chip
   int splits = 1;
   if (D.bf16) {
-    const long tiles = long(ceil_div(D.mrows, 128)) * long(heads);
+    const long tiles = long(ceil_div(D.mrows, 256)) * long(heads);
     const long want = 2L * num_cus;
     while (tiles * splits < want && splits < 64) splits *= 2;
     // at least two 64-key tiles per split
@@ -296,19 +309,35 @@ ScoreWs score_ws_layout(const Dims& D, int num_cus) {
   return L;
 }
 
-hipError_t launch_score_lse(const Dims& P, const ScoreWs& L, const void* k, const void* cent, float* ell,
-                            float* lpart, hipStream_t s) {
+namespace {
+
+template <int D, int BK>
+void launch_lse_bf16(const Dims& P, const ScoreWs& L, const void* k, const void* cent, float* ell, float* lpart,
+                     hipStream_t s) {
+  const int row_tiles = ceil_div(P.mrows, LseCfg<D>::kRows);
+  const int grid = row_tiles * L.splits * P.B * P.H;
+  hipLaunchKernelGGL((score_lse_bf16<D, BK>), dim3(grid), dim3(256), 0, s, P, L.split_keys, L.splits, row_tiles,
+                     static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(cent), ell, lpart);
+}
+
+template <int D>
+void launch_lse_bf16_d(const Dims& P, const ScoreWs& L, const void* k, const void* cent, float* ell, float* lpart,
+                       hipStream_t s) {
+  switch (P.Bk) {
+    case 16: launch_lse_bf16<D, 16>(P, L, k, cent, ell, lpart, s); break;
+    case 32: launch_lse_bf16<D, 32>(P, L, k, cent, ell, lpart, s); break;
+    case 64: launch_lse_bf16<D, 64>(P, L, k, cent, ell, lpart, s); break;
+    default: launch_lse_bf16<D, 128>(P, L, k, cent, ell, lpart, s); break;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_score_lse(const Dims& P, const ScoreWs& L, const void* k, const void* cent, float* ell, float* lpart,
+                            hipStream_t s) {
   if (P.bf16) {
-    const dim3 grid(ceil_div(P.mrows, 128), L.splits, P.B * P.H);
-    if (P.d == 128) {
-      const size_t lds = 2 * LseCfg<128>::kTileBytes;
-      hipLaunchKernelGGL(score_lse_bf16<128>, grid, dim3(256), lds, s, P, L.split_keys, L.splits,
-                         static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(cent), ell, lpart);
-    } else {
-      const size_t lds = 2 * LseCfg<64>::kTileBytes;
-      hipLaunchKernelGGL(score_lse_bf16<64>, grid, dim3(256), lds, s, P, L.split_keys, L.splits,
-                         static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(cent), ell, lpart);
-    }
+    if (P.d == 128) launch_lse_bf16_d<128>(P, L, k, cent, ell, lpart, s);
+    else launch_lse_bf16_d<64>(P, L, k, cent, ell, lpart, s);
   } else {
     const dim3 grid(P.nqb, P.B * P.H);
     if (P.d == 128)
