@@ -12,12 +12,13 @@
 //     its centroid and gets size 0;
 //   * initial centroids are the strided queries x[floor(c*n/C')], C' = min(C, n).
 //
-// One workgroup per (b, h, query block), one thread per query row. Each thread
-// keeps its query in VGPRs and runs eight independent distance chains at once;
-// centroids sit in LDS transposed ([k][c]) so one 16-byte broadcast read feeds
-// four chains. The update uses per-cluster member lists built with wave
-// ballots, so every (cluster, dim) thread only walks its own members, in
-// ascending row order, with no divergence inside a wave.
+// One workgroup per (b, h, query block), two threads per query row: each keeps
+// its query in VGPRs and scans four of every eight clusters with four
+// independent distance chains; the two halves then merge their minima (lower
+// index wins ties). Centroids sit in LDS transposed ([k][c]) so one 16-byte
+// broadcast read feeds the four chains. The update uses per-cluster member
+// lists built with wave ballots, so every (cluster, dim) thread only walks its
+// own members, in ascending row order, reading them from the block's copy in LDS.
 #include "ab_internal.h"
 
 namespace ab {
@@ -25,8 +26,22 @@ namespace {
 
 #pragma clang fp contract(off)
 
+// Each thread keeps one query in VGPRs (bf16 pairs packed, unpacked at use); the
+// block also sits in LDS (its input type) for the centroid update.
 template <bool BF16, int D>
-__global__ __launch_bounds__(128) void kmeans_kernel(Dims P, const void* __restrict__ qv,
+struct QueryRow {
+  static constexpr int kWords = BF16 ? D / 2 : D;
+  uint32_t w[kWords];
+  __device__ __forceinline__ float get(int k) const {
+    if constexpr (BF16) return (k & 1) ? __uint_as_float(w[k >> 1] & 0xFFFF0000u) : __uint_as_float(w[k >> 1] << 16);
+    else return __uint_as_float(w[k]);
+  }
+};
+
+// Two threads per query row: thread t handles row t % Bq and the clusters
+// c = c0 + 4*(t / Bq) + u (u < 4) of every group of 8.
+template <bool BF16, int D>
+__global__ __launch_bounds__(256) void kmeans_kernel(Dims P, const void* __restrict__ qv,
                                                      float* __restrict__ cent,
                                                      uint16_t* __restrict__ cent_bf16,
                                                      int32_t* __restrict__ sizes_out,
@@ -41,19 +56,21 @@ __global__ __launch_bounds__(128) void kmeans_kernel(Dims P, const void* __restr
   const int n = min(Bq, P.N - row0);
   const int Ci = min(C, n);
   const int tid = threadIdx.x;
-  const int nthr = blockDim.x;
+  const int nthr = blockDim.x;  // 2 * Bq
+  const int r_own = tid % Bq, chalf = tid / Bq;
 
   // LDS carve-up
   using elem_t = typename std::conditional<BF16, uint16_t, float>::type;
-  elem_t* X = reinterpret_cast<elem_t*>(smem);                             // [Bq][D]
-  float* mu_t = reinterpret_cast<float*>(smem + size_t(Bq) * D * sizeof(elem_t));  // [D][CP]
-  int* asg = reinterpret_cast<int*>(mu_t + size_t(D) * CP);                 // [Bq]
-  int* list = asg + Bq;                                                     // [Bq]
-  int* cstart = list + Bq;                                                  // [C]
-  int* ccount = cstart + C;                                                 // [C]
+  elem_t* X = reinterpret_cast<elem_t*>(smem);                                       // [Bq][D]
+  float* mu_t = reinterpret_cast<float*>(smem + size_t(Bq) * D * sizeof(elem_t));    // [D][CP]
+  int* asg = reinterpret_cast<int*>(mu_t + size_t(D) * CP);                          // [Bq]
+  int* list = asg + Bq;                                                              // [Bq]
+  int* cstart = list + Bq;                                                           // [C]
+  int* ccount = cstart + C;                                                          // [C]
+  float* pbest = reinterpret_cast<float*>(ccount + C);                               // [Bq] best of the upper half
+  int* pidx = reinterpret_cast<int*>(pbest + Bq);                                    // [Bq]
 
   const elem_t* qsrc = reinterpret_cast<const elem_t*>(qv) + (size_t(bh) * P.N + row0) * D;
-  // stage the query block (16-byte chunks)
   {
     constexpr int EPC = 16 / sizeof(elem_t);
     const int chunks = n * D / EPC;
@@ -62,64 +79,75 @@ __global__ __launch_bounds__(128) void kmeans_kernel(Dims P, const void* __restr
     for (int p = tid; p < chunks; p += nthr) dst[p] = src[p];
   }
   for (int p = tid; p < D * CP; p += nthr) mu_t[p] = 0.0f;
+  // this thread's query, held in VGPRs for every iteration (16-byte global loads)
+  QueryRow<BF16, D> x;
+  {
+    const uint4* src = reinterpret_cast<const uint4*>(qsrc + size_t(min(r_own, n - 1)) * D);
+#pragma unroll
+    for (int c4 = 0; c4 < QueryRow<BF16, D>::kWords / 4; ++c4) {
+      const uint4 u = src[c4];
+      x.w[4 * c4 + 0] = u.x;
+      x.w[4 * c4 + 1] = u.y;
+      x.w[4 * c4 + 2] = u.z;
+      x.w[4 * c4 + 3] = u.w;
+    }
+  }
   __syncthreads();
+  auto xlds = [&](int r, int k) -> float {
+    if constexpr (BF16) return bf16_to_f32(X[r * D + k]); else return X[r * D + k];
+  };
   for (int p = tid; p < Ci * D; p += nthr) {
     const int c = p / D, k = p % D;
-    const int r = (c * n) / Ci;
-    float x;
-    if constexpr (BF16) x = bf16_to_f32(X[r * D + k]); else x = X[r * D + k];
-    mu_t[k * CP + c] = x;
+    mu_t[k * CP + c] = xlds((c * n) / Ci, k);
   }
   if (tid < C) ccount[tid] = 0;
   __syncthreads();
 
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  // this thread's query, held in VGPRs for every iteration (16-byte global loads)
-  float x[D];
-  {
-    constexpr int EPC = 16 / sizeof(elem_t);
-    const uint4* src = reinterpret_cast<const uint4*>(qsrc + size_t(min(tid, n - 1)) * D);
-#pragma unroll
-    for (int c = 0; c < D / EPC; ++c) {
-      const uint4 u = src[c];
-      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-      for (int e = 0; e < EPC; ++e) {
-        if constexpr (BF16) x[c * EPC + e] = bf16_to_f32(uint16_t(w[e >> 1] >> ((e & 1) * 16)));
-        else x[c * EPC + e] = __uint_as_float(w[e]);
-      }
-    }
-  }
   for (int it = 0; it < P.T; ++it) {
-    // ---- assignment ----
-    if (tid < n) {
-      float best = __builtin_inff();
-      int bi = 0;
+    // ---- assignment: each half of the threads scans 4 of every 8 clusters ----
+    float best = __builtin_inff();
+    int bi = 0;
+    if (r_own < n) {
       for (int c0 = 0; c0 < Ci; c0 += 8) {
-        float acc[8];
+        const int cb = c0 + 4 * chalf;
+        float acc[4];
 #pragma unroll
-        for (int cc = 0; cc < 8; ++cc) acc[cc] = 0.0f;
+        for (int cc = 0; cc < 4; ++cc) acc[cc] = 0.0f;
 #pragma unroll
         for (int k = 0; k < D; ++k) {
-          const float4 m0 = *reinterpret_cast<const float4*>(&mu_t[k * CP + c0]);
-          const float4 m1 = *reinterpret_cast<const float4*>(&mu_t[k * CP + c0 + 4]);
-          const float m[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+          const float xk = x.get(k);
+          const float4 m4 = *reinterpret_cast<const float4*>(&mu_t[k * CP + cb]);
+          const float m[4] = {m4.x, m4.y, m4.z, m4.w};
 #pragma unroll
-          for (int cc = 0; cc < 8; ++cc) {
-            const float df = __fsub_rn(x[k], m[cc]);
+          for (int cc = 0; cc < 4; ++cc) {
+            const float df = __fsub_rn(xk, m[cc]);
             acc[cc] = __fadd_rn(acc[cc], __fmul_rn(df, df));
           }
         }
-        const int lim = min(8, Ci - c0);
+        const int lim = min(4, Ci - cb);
         for (int cc = 0; cc < lim; ++cc) {
           if (acc[cc] < best) {
             best = acc[cc];
-            bi = c0 + cc;
+            bi = cb + cc;
           }
         }
       }
-      asg[tid] = bi;
+    }
+    // merge the two halves: the lower cluster index wins ties. Within each half the
+    // scan is in ascending cluster order, but the halves interleave (0-3 | 4-7, 8-11 |
+    // 12-15, ...), so ties are broken by index explicitly.
+    if (chalf == 1 && r_own < n) {
+      pbest[r_own] = best;
+      pidx[r_own] = bi;
+    }
+    __syncthreads();
+    if (chalf == 0 && r_own < n) {
+      const float ob = pbest[r_own];
+      const int oi = pidx[r_own];
+      if (ob < best || (ob == best && oi < bi)) bi = oi;
+      asg[r_own] = bi;
     }
     __syncthreads();
     // ---- member lists (ascending rows per cluster), one wave ----
@@ -141,19 +169,14 @@ __global__ __launch_bounds__(128) void kmeans_kernel(Dims P, const void* __restr
       }
     }
     __syncthreads();
-    // ---- update ----
+    // ---- update: members summed in ascending row order, one correctly rounded division ----
     for (int p = tid; p < Ci * D; p += nthr) {
       const int c = p / D, k = p % D;
       const int cnt = ccount[c];
       if (cnt > 0) {
         const int st = cstart[c];
         float s = 0.0f;
-        for (int m = 0; m < cnt; ++m) {
-          const int r = list[st + m];
-          float x;
-          if constexpr (BF16) x = bf16_to_f32(X[r * D + k]); else x = X[r * D + k];
-          s = __fadd_rn(s, x);
-        }
+        for (int m = 0; m < cnt; ++m) s = __fadd_rn(s, xlds(list[st + m], k));
         mu_t[k * CP + c] = __fdiv_rn(s, float(cnt));
       }
     }
@@ -178,13 +201,13 @@ template <bool BF16, int D>
 hipError_t launch(const Dims& P, const void* q, float* cent, uint16_t* cb, int32_t* sz, uint8_t* as,
                   hipStream_t s) {
   const int CP = (P.C + 7) & ~7;
-  const size_t lds = size_t(P.Bq) * D * (BF16 ? 2 : 4) + size_t(D) * CP * 4 + size_t(P.Bq) * 8 + size_t(P.C) * 8;
+  const size_t lds = size_t(P.Bq) * D * (BF16 ? 2 : 4) + size_t(D) * CP * 4 + size_t(P.Bq) * 16 + size_t(P.C) * 8;
   auto kern = kmeans_kernel<BF16, D>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
   if (e != hipSuccess) return e;
   const int blocks = P.B * P.H * P.nqb;
-  hipLaunchKernelGGL(kern, dim3(blocks), dim3(P.Bq), lds, s, P, q, cent, cb, sz, as);
+  hipLaunchKernelGGL(kern, dim3(blocks), dim3(2 * P.Bq), lds, s, P, q, cent, cb, sz, as);
   return hipGetLastError();
 }
 
