@@ -10,10 +10,15 @@
 //   keep iff u_j < t_j; weight = fp32(2^24) / fp32(t_j)
 // Philox4x32-10 follows Salmon et al., SC'11.
 //
-// One workgroup per row. The capped set is an LDS bitset; each pass is one
-// workgroup reduction of a 64-bit sum. The draw gives each thread one 32-block
-// word of the mask (eight Philox calls), and a workgroup exclusive scan of the
-// per-word popcounts places the kept indices in ascending order.
+// Rows with at most 4096 key sub-blocks (every workload in use): one wave per
+// row, four rows per workgroup, no workgroup barriers. Lane l holds the
+// quantized scores of sub-blocks [1024c + 16l, 1024c + 16l + 16) of every 1024-wide
+// chunk c in VGPRs; each water-filling pass is a wave reduction; the lane draws
+// its own four Philox blocks, computes thresholds with one reciprocal per row
+// and an exact integer fix-up, and a wave prefix sum over the lanes' popcounts
+// places the kept indices in ascending order.
+// Longer rows: one workgroup per row, the capped set in an LDS bitset, scores
+// re-read on every pass.
 #include "ab_internal.h"
 
 namespace ab {
@@ -203,13 +208,181 @@ __global__ __launch_bounds__(kThreads) void sample_kernel(Dims P, int K, uint32_
   if (tid == 0) counts[row] = scan_base;
 }
 
+
+// floor(num / S) for num < 2^64 with quotient below 2^25, given rS ~ 1/S:
+// the fp64 estimate is within one of the true floor, the fix-ups make it exact.
+__device__ __forceinline__ uint32_t floor_div_est(uint64_t num, uint64_t S, double rS) {
+  uint64_t q = uint64_t(double(num) * rS);
+  if (q * S > num) --q;
+  if ((q + 1) * S <= num) ++q;
+  return uint32_t(q);
+}
+
+__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+__device__ __forceinline__ int wave_sum_i32(int v) {
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+constexpr int kLaneElems = 16;          // sub-blocks per lane per chunk
+constexpr int kChunk = 64 * kLaneElems; // sub-blocks per chunk
+
+template <int NCH>
+__global__ __launch_bounds__(256) void sample_wave_kernel(Dims P, int K, int rows, uint32_t seed_lo,
+                                                          uint32_t seed_hi, const float* __restrict__ scores,
+                                                          int32_t* __restrict__ idx, float* __restrict__ weights,
+                                                          int32_t* __restrict__ counts,
+                                                          uint32_t* __restrict__ mask) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;  // the whole wave leaves; nothing below synchronises the workgroup
+  const int nkb = P.nkb;
+  const int i = row % P.nqb;
+  const int bh = row / P.nqb;
+  const int h = bh % P.H, b = bh / P.H;
+  const float* s = scores + size_t(row) * nkb;
+  const bool vec_ok = (nkb & 3) == 0;
+
+  // ---- quantized scores in VGPRs; valid-element masks ----
+  uint32_t w[NCH][kLaneElems];
+  uint32_t valid[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int j0 = c * kChunk + lane * kLaneElems;
+    const int nv = min(kLaneElems, max(0, nkb - j0));
+    valid[c] = (1u << nv) - 1u;  // nv <= 16
+    if (vec_ok && nv == kLaneElems) {
+      const float4* s4 = reinterpret_cast<const float4*>(s + j0);
+#pragma unroll
+      for (int q = 0; q < kLaneElems / 4; ++q) {
+        const float4 v = s4[q];
+        w[c][4 * q + 0] = quantize(v.x);
+        w[c][4 * q + 1] = quantize(v.y);
+        w[c][4 * q + 2] = quantize(v.z);
+        w[c][4 * q + 3] = quantize(v.w);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < kLaneElems; ++e) w[c][e] = (e < nv) ? quantize(s[j0 + e]) : 0u;
+    }
+  }
+
+  // ---- integer water-filling (capped bits per chunk) ----
+  uint32_t cap[NCH];
+  uint64_t room = 0, S = 1;
+  if (K >= nkb) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) cap[c] = valid[c];
+  } else {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) cap[c] = 0u;
+    int m = 0;
+    for (;;) {
+      uint32_t part = 0;  // at most 64 values below 2^25
+#pragma unroll
+      for (int c = 0; c < NCH; ++c)
+#pragma unroll
+        for (int e = 0; e < kLaneElems; ++e) part += ((cap[c] >> e) & 1u) ? 0u : w[c][e];
+      S = wave_sum_u64(uint64_t(part));
+      room = uint64_t(K - m);
+      int nnew = 0;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+#pragma unroll
+        for (int e = 0; e < kLaneElems; ++e) {
+          const bool un = ((valid[c] & ~cap[c]) >> e) & 1u;
+          if (un && room * uint64_t(w[c][e]) >= S) {
+            cap[c] |= 1u << e;
+            ++nnew;
+          }
+        }
+      }
+      nnew = wave_sum_i32(nnew);
+      if (nnew == 0) break;
+      m += nnew;
+    }
+  }
+
+  // ---- draw: thresholds replace the weights in place ----
+  const double rS = 1.0 / double(S);
+  uint32_t keep[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    keep[c] = 0u;
+    const int g0 = (c * kChunk + lane * kLaneElems) >> 2;
+#pragma unroll
+    for (int g = 0; g < kLaneElems / 4; ++g) {
+      if (!((valid[c] >> (4 * g)) & 0xFu)) continue;
+      const uint4 r = philox4x32_10(uint32_t(g0 + g), uint32_t(i), uint32_t(h), uint32_t(b), seed_lo, seed_hi);
+      const uint32_t rr[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const int e = 4 * g + e4;
+        uint32_t t = kOne;
+        if (!((cap[c] >> e) & 1u)) {
+          const uint32_t q = floor_div_est(room * uint64_t(w[c][e]) * uint64_t(kOne), S, rS);
+          t = q > 0u ? q : 1u;
+        }
+        w[c][e] = t;
+        if (((valid[c] >> e) & 1u) && (rr[e4] >> 8) < t) keep[c] |= 1u << e;
+      }
+    }
+  }
+
+  // ---- compaction in ascending sub-block order: chunk, then lane, then element ----
+  const size_t out0 = size_t(row) * nkb;
+  const int words = ceil_div(nkb, 32);
+  int base = 0;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int pc = __popc(keep[c]);
+    int incl = pc;
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += y;
+    }
+    int pos = base + incl - pc;
+    const int j0 = c * kChunk + lane * kLaneElems;
+#pragma unroll
+    for (int e = 0; e < kLaneElems; ++e) {
+      if ((keep[c] >> e) & 1u) {
+        idx[out0 + pos] = j0 + e;
+        weights[out0 + pos] = __fdiv_rn(16777216.0f, float(w[c][e]));
+        ++pos;
+      }
+    }
+    base += __shfl(incl, 63, 64);
+    if (mask) {
+      const uint32_t hi = __shfl_down(keep[c], 1, 64);
+      const int wd = (c * kChunk) / 32 + lane / 2;
+      if (!(lane & 1) && wd < words) mask[size_t(row) * words + wd] = keep[c] | (hi << 16);
+    }
+  }
+  if (lane == 0) counts[row] = base;
+}
+
 }  // namespace
 
 hipError_t launch_sample(const Dims& P, const float* scores, int K, uint64_t seed, int32_t* idx, float* weights,
                          int32_t* counts, uint32_t* mask, hipStream_t s) {
-  const size_t lds = size_t(ceil_div(P.nkb, 32)) * 4;
-  hipLaunchKernelGGL(sample_kernel, dim3(P.B * P.H * P.nqb), dim3(kThreads), lds, s, P, K, uint32_t(seed),
-                     uint32_t(seed >> 32), scores, idx, weights, counts, mask);
+  const int rows = P.B * P.H * P.nqb;
+  const uint32_t lo = uint32_t(seed), hi = uint32_t(seed >> 32);
+  const int nch = ceil_div(P.nkb, kChunk);
+  const dim3 grid(ceil_div(rows, 4)), block(256);
+  switch (nch) {
+    case 1: hipLaunchKernelGGL(sample_wave_kernel<1>, grid, block, 0, s, P, K, rows, lo, hi, scores, idx, weights, counts, mask); break;
+    case 2: hipLaunchKernelGGL(sample_wave_kernel<2>, grid, block, 0, s, P, K, rows, lo, hi, scores, idx, weights, counts, mask); break;
+    case 3: hipLaunchKernelGGL(sample_wave_kernel<3>, grid, block, 0, s, P, K, rows, lo, hi, scores, idx, weights, counts, mask); break;
+    case 4: hipLaunchKernelGGL(sample_wave_kernel<4>, grid, block, 0, s, P, K, rows, lo, hi, scores, idx, weights, counts, mask); break;
+    default: {
+      const size_t lds = size_t(ceil_div(P.nkb, 32)) * 4;
+      hipLaunchKernelGGL(sample_kernel, dim3(rows), dim3(kThreads), lds, s, P, K, lo, hi, scores, idx, weights,
+                         counts, mask);
+    }
+  }
   return hipGetLastError();
 }
 

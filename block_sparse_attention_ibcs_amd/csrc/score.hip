@@ -243,6 +243,11 @@ __global__ __launch_bounds__(256) void score_lse_f32(Dims P, const float* __rest
   }
 }
 
+// s_j = sum_c (|cluster c| / n) 2^(ell_jc - L_c), L_c the row's base-2
+// log-sum-exp over all keys, ascending c, empty clusters skipped. CT is the
+// cluster count when it is fixed at compile time (float4 loads of the C values
+// of a sub-block, four sub-blocks in flight per thread), 0 for any count.
+template <int CT>
 __global__ __launch_bounds__(256) void score_assemble(Dims P, int splits, const float* __restrict__ ell,
                                                       const float* __restrict__ lpart,
                                                       const int32_t* __restrict__ sizes,
@@ -250,8 +255,9 @@ __global__ __launch_bounds__(256) void score_assemble(Dims P, int splits, const 
   __shared__ float Lc[128], wc[128];
   const int blk = blockIdx.x;  // (b*H + h)*nqb + i
   const int i = blk % P.nqb, bh = blk / P.nqb;
-  const int C = P.C;
+  const int C = CT > 0 ? CT : P.C;
   const int n = min(P.Bq, P.N - i * P.Bq);
+  const int nkb = P.nkb;
   for (int c = threadIdx.x; c < C; c += blockDim.x) {
     const float* lp = lpart + (size_t(bh) * P.mrows + i * C + c) * splits;
     float m = -__builtin_inff();
@@ -262,15 +268,46 @@ __global__ __launch_bounds__(256) void score_assemble(Dims P, int splits, const 
     wc[c] = float(sizes[size_t(blk) * C + c]) / float(n);
   }
   __syncthreads();
-  const float* eb = ell + size_t(blk) * P.nkb * C;
-  float* out = scores + size_t(blk) * P.nkb;
-  for (int j = threadIdx.x; j < P.nkb; j += blockDim.x) {
-    float s = 0.0f;
-    for (int c = 0; c < C; ++c) {
-      const float w = wc[c];
-      if (w > 0.0f) s += w * fast_exp2(eb[size_t(j) * C + c] - Lc[c]);
+  const float* eb = ell + size_t(blk) * nkb * C;
+  float* out = scores + size_t(blk) * nkb;
+  if constexpr (CT > 0) {
+    constexpr int C4 = CT / 4;
+    constexpr int U = 4;
+    const float4* eb4 = reinterpret_cast<const float4*>(eb);
+    for (int j0 = 0; j0 < nkb; j0 += U * 256) {
+      float4 e[U][C4];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int j = min(j0 + u * 256 + int(threadIdx.x), nkb - 1);
+#pragma unroll
+        for (int q = 0; q < C4; ++q) e[u][q] = eb4[size_t(j) * C4 + q];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float s = 0.0f;
+#pragma unroll
+        for (int q = 0; q < C4; ++q) {
+          const float x[4] = {e[u][q].x, e[u][q].y, e[u][q].z, e[u][q].w};
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const float w = wc[4 * q + t];
+            const float v = w * fast_exp2(x[t] - Lc[4 * q + t]);
+            s += (w > 0.0f) ? v : 0.0f;
+          }
+        }
+        const int j = j0 + u * 256 + int(threadIdx.x);
+        if (j < nkb) out[j] = s;
+      }
     }
-    out[j] = s;
+  } else {
+    for (int j = threadIdx.x; j < nkb; j += blockDim.x) {
+      float s = 0.0f;
+      for (int c = 0; c < C; ++c) {
+        const float w = wc[c];
+        if (w > 0.0f) s += w * fast_exp2(eb[size_t(j) * C + c] - Lc[c]);
+      }
+      out[j] = s;
+    }
   }
 }
 
@@ -352,8 +389,13 @@ hipError_t launch_score_lse(const Dims& P, const ScoreWs& L, const void* k, cons
 
 hipError_t launch_score_assemble(const Dims& P, const ScoreWs& L, const float* ell, const float* lpart,
                                  const int32_t* sizes, float* scores, hipStream_t s) {
-  hipLaunchKernelGGL(score_assemble, dim3(P.B * P.H * P.nqb), dim3(256), 0, s, P, L.splits, ell, lpart, sizes,
-                     scores);
+  const dim3 grid(P.B * P.H * P.nqb), block(256);
+  switch (P.C) {
+    case 4: hipLaunchKernelGGL(score_assemble<4>, grid, block, 0, s, P, L.splits, ell, lpart, sizes, scores); break;
+    case 8: hipLaunchKernelGGL(score_assemble<8>, grid, block, 0, s, P, L.splits, ell, lpart, sizes, scores); break;
+    case 16: hipLaunchKernelGGL(score_assemble<16>, grid, block, 0, s, P, L.splits, ell, lpart, sizes, scores); break;
+    default: hipLaunchKernelGGL(score_assemble<0>, grid, block, 0, s, P, L.splits, ell, lpart, sizes, scores);
+  }
   return hipGetLastError();
 }
 

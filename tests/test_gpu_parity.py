@@ -296,6 +296,51 @@ def test_edge_shapes(N, H, d, Bq, Bk, C, T, density):
             assert np.linalg.norm(run.out[0, h] - o) / np.linalg.norm(o) <= 1e-2
 
 
+@pytest.mark.parametrize("nkb,density", [(37, 0.3), (1024, 0.1), (1000, 1.0), (1500, 0.02), (2363, 0.1),
+                                         (4096, 0.5), (4100, 0.1), (9000, 0.05)])
+def test_sampler_rows_any_length(nkb, density):
+    """The sampler alone on synthetic score rows: short rows, each register-resident
+    row length class, and rows long enough for the LDS-bitset path; peaked rows force
+    several water-filling passes; zero, negative, NaN, sub-2^-24 and >= 1 scores."""
+    _gpu()
+    Bk, Bq, H = 16, 128, 2
+    N = nkb * Bk - 3  # ragged last sub-block
+    desc = ab.Desc(1, H, N, 128, ab.AB_BF16, Bq, Bk, 8)
+    assert desc.nkb == nkb
+    rng = np.random.default_rng(nkb)
+    shape = (1, H, desc.nqb, nkb)
+    logits = rng.standard_normal(shape) * 2.0
+    peak = rng.random(shape) < 8.0 / nkb
+    logits[peak] += 12.0
+    sc = np.exp(logits - logits.max(axis=-1, keepdims=True))
+    sc = (sc / sc.sum(axis=-1, keepdims=True)).astype(np.float32)
+    flat = sc.reshape(-1, nkb)
+    r = rng.integers(0, flat.shape[0], size=6)
+    flat[r[0], : min(nkb, 5)] = 0.0
+    flat[r[1], 1 % nkb] = -0.5
+    flat[r[2], 2 % nkb] = np.nan
+    flat[r[3], 3 % nkb] = 2.0**-30
+    flat[r[4], 4 % nkb] = 1.0
+    flat[r[5], 0] = 3.0
+    scores_d = torch.from_numpy(sc).cuda()
+    seed = 0xABCDEF0123 + nkb
+    idx_d, wts_d, cnt_d, mask_d = ab.ab_sample(desc, scores_d, density, seed)
+    torch.cuda.synchronize()
+    idx, wts, cnt = idx_d.cpu().numpy(), wts_d.cpu().numpy(), cnt_d.cpu().numpy()
+    mask = mask_d.cpu().numpy().view(np.uint32)
+    keys = [(0, int(x) // desc.nqb, int(x) % desc.nqb) for x in r] + [(0, 0, 0), (0, H - 1, desc.nqb - 1)]
+    ref = sample_rows(sc, density, seed, keys)
+    for key, o in ref.items():
+        b, h, i = key
+        c = int(cnt[b, h, i])
+        assert c == o["count"], key
+        assert np.array_equal(idx[b, h, i, :c], o["idx"]), key
+        assert np.array_equal(wts[b, h, i, :c].view(np.uint32), o["weight"].view(np.uint32)), key
+        assert np.array_equal(mask[b, h, i], o["mask"]), key
+    bits = np.unpackbits(mask.view(np.uint8), axis=-1, bitorder="little").sum(axis=-1)
+    assert np.array_equal(bits, cnt)
+
+
 def test_empty_rows_give_zero_output():
     run = _run("tiny", density=0.25)
     cnt = run.cnt_d.clone()
