@@ -80,6 +80,11 @@ int32_t make_dims(const ab_desc* d, ab::Dims* P) {
   D.bf16 = d->dtype == AB_BF16;
   D.scale = (d->scale > 0.0f && std::isfinite(d->scale)) ? d->scale : float(1.0 / std::sqrt(double(D.d)));
   if (D.nkb > kMaxNkb) return fail(AB_ERR_SHAPE, "N/k_block = %d sub-blocks exceeds %d", D.nkb, kMaxNkb);
+  // Kernels address one head's K or V with 32-bit buffer offsets and use 2^31 as
+  // an always-out-of-range offset, so one head must stay below 2 GiB.
+  const int64_t head_bytes = int64_t(D.N) * D.d * (D.bf16 ? 2 : 4);
+  if (head_bytes >= (int64_t(1) << 31))
+    return fail(AB_ERR_SHAPE, "one head of K/V takes %lld bytes, the limit is 2^31 - 1", (long long)head_bytes);
   return AB_OK;
 }
 

@@ -49,7 +49,8 @@ extern "C" {
 /* Return codes. */
 #define AB_OK 0
 #define AB_ERR_NULL (-1)      /* a required pointer is NULL */
-#define AB_ERR_SHAPE (-2)     /* B, H, N < 1, d not in {64, 128}, or sizes overflow */
+#define AB_ERR_SHAPE (-2)     /* B, H, N < 1, d not in {64, 128}, or sizes overflow (one head of K
+                                 or V must take less than 2^31 bytes) */
 #define AB_ERR_PARAM (-3)     /* q_block, k_block, n_clusters or kmeans_iters out of range */
 #define AB_ERR_DENSITY (-4)   /* density not in (0, 1] (NaN included) */
 #define AB_ERR_DTYPE (-5)     /* dtype is not AB_BF16 or AB_F32 */

@@ -77,6 +77,8 @@ def test_workspace_size_covers_tables():
         (dict(kmeans_iters=0), -3),
         (dict(kmeans_iters=65), -3),
         (dict(N=1 << 25), -2),
+        (dict(N=1 << 23, k_block=128), -2),  # one bf16 d=128 head of K is 2 GiB
+        (dict(N=1 << 22, k_block=128, dtype=1), -2),  # one fp32 d=128 head is 2 GiB
     ],
 )
 def test_validation_errors(kw, code):
