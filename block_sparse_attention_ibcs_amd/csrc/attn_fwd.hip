@@ -32,7 +32,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kSlots = 64;
 
-template <int D, int BQ>
+template <int D, int BQ, int BK>
 struct AttnCfg {
   static constexpr int kWaves = BQ / 32;           // each wave owns 32 query rows
   static constexpr int kThreads = kWaves * 64;
@@ -42,6 +42,11 @@ struct AttnCfg {
   static constexpr int kLoadsPerTile = kTileBytes / 1024;     // 64 lanes x 16 bytes per load
   static constexpr int kLoadsPerWave = kLoadsPerTile / kWaves;
   static constexpr int kSlotsPerLoad = 1024 / kRowBytes;      // 4 or 8: within one sub-block
+  static constexpr int kWaveSlots = kSlots / kWaves;          // consecutive slots gathered by one wave
+  static constexpr int kWaveEntries = BK >= kWaveSlots ? 1 : kWaveSlots / BK;  // sub-blocks per wave
+  static constexpr int kTileEntries = BK >= kSlots ? 1 : kSlots / BK;         // sub-blocks per tile
+  static constexpr int kEntryShift = __builtin_ctz(BK * kRowBytes);            // sub-block -> byte offset
+  static_assert(kSlotsPerLoad <= BK, "one gather load must stay inside one sub-block");
 };
 
 // Tiles are unpadded [slot][d] rows whose 16-byte chunks are permuted by an XOR
@@ -57,14 +62,19 @@ __device__ __forceinline__ int v_swz(int slot) {
   return D == 128 ? ((slot & 3) << 2) : (((slot >> 1) & 1) << 2);
 }
 
-template <int D, int BQ>
+// Sub-block of tile-relative slot s (s < 64): its index among the tile's entries.
+template <int BK>
+__device__ __forceinline__ constexpr int slot_entry(int s) {
+  return BK >= kSlots ? 0 : s / BK;
+}
+
+template <int D, int BQ, int BK>
 __global__ __launch_bounds__(BQ * 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_bf16(Dims P, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                    const uint16_t* __restrict__ v, const int32_t* __restrict__ idx,
                    const float* __restrict__ weights, const int32_t* __restrict__ counts,
                    uint16_t* __restrict__ out, float* __restrict__ lse) {
-  using Cfg = AttnCfg<D, BQ>;
-  constexpr uint32_t kOOB = 0x80000000u;  // beyond every buffer: the hardware returns zeros
+  using Cfg = AttnCfg<D, BQ, BK>;
   // Four separate LDS objects (K and V, two stages each): the compiler can then tell
   // that the gather landing in one stage does not alias the reads of the other, and
   // keeps its vector-memory waits out of the math.
@@ -73,17 +83,18 @@ void attn_fwd_bf16(Dims P, const uint16_t* __restrict__ q, const uint16_t* __res
   __shared__ __align__(16) unsigned char v0s[Cfg::kTileBytes];
   __shared__ __align__(16) unsigned char v1s[Cfg::kTileBytes];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, col = lane & 31;
   const int blk = xcd_remap(blockIdx.x, gridDim.x);  // (b*H + h)*nqb + i
   const int i = blk % P.nqb, bh = blk / P.nqb;
-  const int N = P.N, Bk = P.Bk;
-  const int bk_shift = __builtin_ctz(Bk);
+  const int N = P.N;
   const int row0 = i * BQ;
   const int n = min(BQ, N - row0);
   const int cnt = counts[blk];
   const int32_t* list = idx + size_t(blk) * P.nkb;
   const float* wl = weights + size_t(blk) * P.nkb;
+  // one head of K or V; rows at or beyond N read as zeros (buffer range check)
   const int head_bytes = N * Cfg::kRowBytes;
   const __amdgpu_buffer_rsrc_t rk =
       __builtin_amdgcn_make_buffer_rsrc((void*)(k + size_t(bh) * N * D), (short)0, head_bytes, 0x00020000);
@@ -111,63 +122,66 @@ void attn_fwd_bf16(Dims P, const uint16_t* __restrict__ q, const uint16_t* __res
   // key slots: the kept sub-blocks laid end to end; the ragged tail block (always the
   // last entry when kept) leaves its padding at the very end, so slot gs holds a real
   // key iff gs < vend
-  const int total = cnt << bk_shift;
+  const int total = cnt * BK;
   const int ntiles = ceil_div(total, kSlots);
-  const int tail_pad = (cnt > 0 && list[cnt - 1] == P.nkb - 1) ? (P.nkb << bk_shift) - N : 0;
+  const int tail_pad = (cnt > 0 && list[cnt - 1] == P.nkb - 1) ? P.nkb * BK - N : 0;
   const int vend = total - tail_pad;
 
-  // Kept-list entries and weights are fetched ahead with unconditional (clamped)
-  // loads whose results are only consumed in a later iteration, so no wait on them
-  // ever sits between a tile's gather and its math.
-  // entries(t): the list entry of each of this wave's loads of tile t; one load covers
-  // kSlotsPerLoad consecutive slots of a single sub-block.
-  // Both go through buffer (vector-memory) loads: a scalar load would share its wait
-  // counter with the LDS reads of the math and stall them.
+  // Kept-list entries and weights are fetched ahead with unconditional loads clamped
+  // to the list, whose results are only consumed in a later iteration, so no wait on
+  // them ever sits between a tile's gather and its math. Slots past the list end thus
+  // gather a real sub-block again; the last tile masks them. Both go through buffer
+  // (vector-memory) loads: a scalar load would share its wait counter with the LDS
+  // reads of the math and stall them.
   const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc((void*)list, (short)0, P.nkb * 4, 0x00020000);
   const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void*)wl, (short)0, P.nkb * 4, 0x00020000);
-  auto entries = [&](int t, int (&kv)[Cfg::kLoadsPerWave]) {
+  // entries(t): the sub-blocks this wave gathers for tile t
+  auto entries = [&](int t, int (&kv)[Cfg::kWaveEntries]) {
+    const int ord0 = (t * kSlots + wave * Cfg::kWaveSlots) / BK;
+#pragma unroll
+    for (int e = 0; e < Cfg::kWaveEntries; ++e)
+      kv[e] = __builtin_amdgcn_raw_buffer_load_b32(rl, uint32_t(min(ord0 + e, cnt - 1)) * 4, 0, 0);
+  };
+  // weights of the sub-blocks of tile t
+  auto tile_weights = [&](int t, float (&wv)[Cfg::kTileEntries]) {
+    const int ord0 = (t * kSlots) / BK;
+#pragma unroll
+    for (int e = 0; e < Cfg::kTileEntries; ++e)
+      wv[e] = __builtin_bit_cast(float,
+                                 __builtin_amdgcn_raw_buffer_load_b32(rw, uint32_t(min(ord0 + e, cnt - 1)) * 4, 0, 0));
+  };
+  // Per-lane constant part of each gather load's byte offset: the key row inside its
+  // sub-block and the permuted 16-byte chunk. The sub-block part is added per tile.
+  uint32_t kofs[Cfg::kLoadsPerWave], vofs[Cfg::kLoadsPerWave];
+#pragma unroll
+  for (int j = 0; j < Cfg::kLoadsPerWave; ++j) {
+    const int slot = wave * Cfg::kWaveSlots + j * Cfg::kSlotsPerLoad + lane / Cfg::kChunks;  // row in the tile
+    const int within = slot % BK;  // row inside its sub-block (tiles start on sub-block bounds for BK <= 64)
+    const int pos = lane % Cfg::kChunks;
+    kofs[j] = uint32_t(within * Cfg::kRowBytes + ((pos ^ k_swz<D>(slot)) << 4));
+    vofs[j] = uint32_t(within * Cfg::kRowBytes + ((pos ^ v_swz<D>(slot)) << 4));
+  }
+  // asynchronous gather of tile t straight into LDS (no VGPR staging)
+  auto issue_tile = [&](int t, unsigned char* kdst, unsigned char* vdst, const int (&kv)[Cfg::kWaveEntries]) {
+    // a 128-key sub-block spans two tiles: odd tiles take its second half
+    const uint32_t hoff = BK > kSlots ? uint32_t((t * kSlots) % BK) * Cfg::kRowBytes : 0u;
 #pragma unroll
     for (int j = 0; j < Cfg::kLoadsPerWave; ++j) {
-      const int ord = (t * kSlots + (wave * Cfg::kLoadsPerWave + j) * Cfg::kSlotsPerLoad) >> bk_shift;
-      kv[j] = __builtin_amdgcn_raw_buffer_load_b32(rl, uint32_t(min(ord, cnt - 1)) * 4, 0, 0);
-    }
-  };
-  // weights(t): slot s of tile t belongs to entry (t*64 + s) >> shift, so a tile
-  // touches at most 64/Bk (<= 4) consecutive entries
-  auto weights4 = [&](int t, float (&wv)[4]) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      wv[j] = __builtin_bit_cast(
-          float, __builtin_amdgcn_raw_buffer_load_b32(rw, uint32_t(min(((t * kSlots) >> bk_shift) + j, cnt - 1)) * 4, 0, 0));
-  };
-  // asynchronous gather of tile t straight into LDS buffer `buf` (no VGPR staging)
-  auto issue_tile = [&](int t, unsigned char* kdst, unsigned char* vdst, const int (&kv)[Cfg::kLoadsPerWave]) {
-#pragma unroll
-    for (int j = 0; j < Cfg::kLoadsPerWave; ++j) {
+      const int e = Cfg::kWaveEntries == 1 ? 0 : (j * Cfg::kSlotsPerLoad) / BK;
+      const uint32_t sb = (uint32_t(kv[e]) << Cfg::kEntryShift) + hoff;
       const int ld = wave * Cfg::kLoadsPerWave + j;
-      const int gs0 = t * kSlots + ld * Cfg::kSlotsPerLoad;
-      const int ord = gs0 >> bk_shift;
-      const int key0 = (ord < cnt) ? (kv[j] << bk_shift) + (gs0 & (Bk - 1)) : N;
-      const int slot = ld * Cfg::kSlotsPerLoad + lane / Cfg::kChunks;
-      const int key = key0 + lane / Cfg::kChunks;
-      const int pos = lane % Cfg::kChunks;
-      const uint32_t base = (key < N) ? uint32_t(key) * Cfg::kRowBytes : kOOB;
-      buffer_load_lds16(rk, kdst + ld * 1024, base + ((pos ^ k_swz<D>(slot)) << 4));
-      buffer_load_lds16(rv, vdst + ld * 1024, base + ((pos ^ v_swz<D>(slot)) << 4));
+      buffer_load_lds16(rk, kdst + ld * 1024, sb + kofs[j]);
+      buffer_load_lds16(rv, vdst + ld * 1024, sb + vofs[j]);
     }
   };
-  // log2 weight of this lane's keys e in [4g, 4g + 4) of half g / 4 (slots
-  // (g/4)*32 + (g%4)*8 + ...), from the four entry weights of tile t
-  auto tile_lw = [&](int t, const float (&wv)[4], float (&lwg)[8]) {
-    float e4[4];
-    const int ord0 = (t * kSlots) >> bk_shift;
+  // log2 weight of each of this lane's eight 4-slot groups (tile slots
+  // (g/4)*32 + (g%4)*8 + half*4 + [0, 4))
+  auto tile_lw = [&](const float (&wv)[Cfg::kTileEntries], float (&lwg)[8]) {
+    float le[Cfg::kTileEntries];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) e4[j] = (ord0 + j < cnt) ? __builtin_amdgcn_logf(wv[j]) : -__builtin_inff();
+    for (int e = 0; e < Cfg::kTileEntries; ++e) le[e] = __builtin_amdgcn_logf(wv[e]);
 #pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      const int jl = ((g >> 2) * 32 + (g & 3) * 8) >> bk_shift;
-      lwg[g] = jl == 0 ? e4[0] : jl == 1 ? e4[1] : jl == 2 ? e4[2] : e4[3];
-    }
+    for (int g = 0; g < 8; ++g) lwg[g] = le[slot_entry<BK>((g >> 2) * 32 + (g & 3) * 8)];
   };
 
   // LDS byte offsets of this lane's fragment reads (independent of the tile)
@@ -185,14 +199,14 @@ void attn_fwd_bf16(Dims P, const uint16_t* __restrict__ q, const uint16_t* __res
     voff[db] = tr_slot * Cfg::kRowBytes + ((((byte >> 4) ^ v_swz<D>(tr_slot)) << 4) | (byte & 15));
   }
 
-  int kv[Cfg::kLoadsPerWave];
-  float wv[4];
+  int kv[Cfg::kWaveEntries];
+  float wv[Cfg::kTileEntries];
   if (ntiles > 0) {
     entries(0, kv);
     __builtin_amdgcn_s_waitcnt(0);
     issue_tile(0, k0s, v0s, kv);
     if (ntiles > 1) entries(1, kv);
-    weights4(0, wv);
+    tile_weights(0, wv);
   }
   // Drain every load issued so far (the Q fragments included) so the compiler's
   // wait-count analysis does not keep waits on them inside the loop.
@@ -203,10 +217,10 @@ void attn_fwd_bf16(Dims P, const uint16_t* __restrict__ q, const uint16_t* __res
     __builtin_amdgcn_s_waitcnt(0);  // this wave's gather of tile t has landed in LDS
     __syncthreads();                // ... and every other wave's; tile t-1 is fully consumed
     float lwg[8];
-    tile_lw(t, wv, lwg);
+    tile_lw(wv, lwg);
     if (t + 1 < ntiles) issue_tile(t + 1, kn, vn, kv);  // lands while tile t is computed
     if (t + 2 < ntiles) entries(t + 2, kv);
-    if (t + 1 < ntiles) weights4(t + 1, wv);
+    if (t + 1 < ntiles) tile_weights(t + 1, wv);
     // S^T for both 32-slot halves, as two independent accumulation chains
     f32x16_t acc[2];
 #pragma unroll
@@ -380,13 +394,24 @@ __global__ __launch_bounds__(128) void attn_fwd_f32(Dims P, const float* __restr
   }
 }
 
-template <int D, int BQ>
+template <int D, int BQ, int BK>
 hipError_t launch_bf16(const Dims& P, const void* q, const void* k, const void* v, const int32_t* idx,
                        const float* weights, const int32_t* counts, void* out, float* lse, hipStream_t s) {
-  hipLaunchKernelGGL((attn_fwd_bf16<D, BQ>), dim3(P.B * P.H * P.nqb), dim3(AttnCfg<D, BQ>::kThreads), 0, s, P,
-                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
-                     idx, weights, counts, static_cast<uint16_t*>(out), lse);
+  hipLaunchKernelGGL((attn_fwd_bf16<D, BQ, BK>), dim3(P.B * P.H * P.nqb), dim3(AttnCfg<D, BQ, BK>::kThreads), 0, s,
+                     P, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                     static_cast<const uint16_t*>(v), idx, weights, counts, static_cast<uint16_t*>(out), lse);
   return hipGetLastError();
+}
+
+template <int D, int BQ>
+hipError_t launch_bf16_bk(const Dims& P, const void* q, const void* k, const void* v, const int32_t* idx,
+                          const float* weights, const int32_t* counts, void* out, float* lse, hipStream_t s) {
+  switch (P.Bk) {
+    case 16: return launch_bf16<D, BQ, 16>(P, q, k, v, idx, weights, counts, out, lse, s);
+    case 32: return launch_bf16<D, BQ, 32>(P, q, k, v, idx, weights, counts, out, lse, s);
+    case 64: return launch_bf16<D, BQ, 64>(P, q, k, v, idx, weights, counts, out, lse, s);
+    default: return launch_bf16<D, BQ, 128>(P, q, k, v, idx, weights, counts, out, lse, s);
+  }
 }
 
 }  // namespace
@@ -394,10 +419,10 @@ hipError_t launch_bf16(const Dims& P, const void* q, const void* k, const void* 
 hipError_t launch_attn_fwd(const Dims& P, const void* q, const void* k, const void* v, const int32_t* idx,
                            const float* weights, const int32_t* counts, void* out, float* lse, hipStream_t s) {
   if (P.bf16) {
-    if (P.d == 128 && P.Bq == 128) return launch_bf16<128, 128>(P, q, k, v, idx, weights, counts, out, lse, s);
-    if (P.d == 128) return launch_bf16<128, 64>(P, q, k, v, idx, weights, counts, out, lse, s);
-    if (P.Bq == 128) return launch_bf16<64, 128>(P, q, k, v, idx, weights, counts, out, lse, s);
-    return launch_bf16<64, 64>(P, q, k, v, idx, weights, counts, out, lse, s);
+    if (P.d == 128 && P.Bq == 128) return launch_bf16_bk<128, 128>(P, q, k, v, idx, weights, counts, out, lse, s);
+    if (P.d == 128) return launch_bf16_bk<128, 64>(P, q, k, v, idx, weights, counts, out, lse, s);
+    if (P.Bq == 128) return launch_bf16_bk<64, 128>(P, q, k, v, idx, weights, counts, out, lse, s);
+    return launch_bf16_bk<64, 64>(P, q, k, v, idx, weights, counts, out, lse, s);
   }
   const dim3 grid(P.B * P.H * P.nqb);
   auto Q = static_cast<const float*>(q);
