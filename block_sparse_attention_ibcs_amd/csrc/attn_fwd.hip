@@ -19,9 +19,10 @@
 // and 16 keys: the row max and row sum need one exchange between the two wave
 // halves, and the probabilities are already in the B-operand layout of
 // O^T += V^T P^T. The weight enters as log2(w_j) added to the logits of block
-// j's keys, which multiplies numerator and denominator alike while keeping
-// every probability in [0, 1]. V is stored transposed in LDS so each lane's A
-// operand is two 8-byte reads.
+// j's keys, which multiplies numerator and denominator alike. The softmax
+// reference is moved only when a row's sum of exponentials overflows its bound,
+// so most tiles need no max pass. V is read from its natural [slot][d] layout
+// with transposing LDS reads, two 8-byte reads per A operand.
 #include "ab_internal.h"
 #include "mfma.h"
 
@@ -244,51 +245,57 @@ void attn_fwd_bf16(Dims P, const uint16_t* __restrict__ q, const uint16_t* __res
           if (gs >= vend) acc[hb][e] = -__builtin_inff();
         }
     }
-    // Upper bound of the tile's weighted logits per row; the running max m is moved
-    // (and O, l rescaled) only when the bound exceeds it by more than 8, so every
-    // probability stays in [0, 2^8].
-    float amax = acc[0][0];
+    // Probabilities 2^(x - m) against the running reference m, packed to bf16, and
+    // the row sum. The reference is only moved (O and l rescaled, the tile redone)
+    // when a row sum is not finite or passes 2^64: on a row's first tile (m = -inf)
+    // and when the logits grow by more than about 64 - 6 in log2 units. Values up to
+    // 2^64 are exact enough (relative rounding does not depend on magnitude) and keep
+    // O and l far from overflow.
+    bf16x8_t pb[4];
+    float ps;
+    auto probs = [&]() {
+      ps = 0.0f;
 #pragma unroll
-    for (int e = 1; e < 16; ++e) amax = fmaxf(amax, acc[0][e]);
+      for (int g = 0; g < 8; ++g) {
+        const float bias = lwg[g] - m;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) amax = fmaxf(amax, acc[1][e]);
-    float lwmax = lwg[0];
+        for (int e = 0; e < 4; ++e) {
+          const float x = fast_exp2(__builtin_fmaf(acc[g >> 2][(g & 3) * 4 + e], c2, bias));
+          pb[g >> 1][(g & 1) * 4 + e] = __bf16(x);
+          ps += x;
+        }
+      }
+      ps = pair_sum(ps);
+    };
+    probs();
+    if (__builtin_amdgcn_ballot_w64(!(ps <= 1.8446744e19f)) != 0) {
+      float amax = acc[0][0];
 #pragma unroll
-    for (int g = 1; g < 8; ++g) lwmax = fmaxf(lwmax, lwg[g]);
-    const float ub = pair_max(__builtin_fmaf(amax, c2, lwmax));  // finite: slot 0 of a tile is a real key
-    if (__builtin_amdgcn_ballot_w64(ub > m + 8.0f) != 0) {
-      const float mn = fmaxf(m, ub);
+      for (int e = 1; e < 16; ++e) amax = fmaxf(amax, acc[0][e]);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) amax = fmaxf(amax, acc[1][e]);
+      float lwmax = lwg[0];
+#pragma unroll
+      for (int g = 1; g < 8; ++g) lwmax = fmaxf(lwmax, lwg[g]);
+      // every row has a real key in slot 0 of the tile, so the bound is finite
+      const float mn = fmaxf(m, pair_max(__builtin_fmaf(amax, c2, lwmax)));
       const float alpha = fast_exp2(m - mn);  // 0 on the first tile (m = -inf)
       l *= alpha;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
       m = mn;
+      probs();
     }
-    // probabilities (written over the logits) and the row sum
-    float ps = 0.0f;
-#pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      const float bias = lwg[g] - m;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float x = fast_exp2(__builtin_fmaf(acc[g >> 2][(g & 3) * 4 + e], c2, bias));
-        acc[g >> 2][(g & 3) * 4 + e] = x;
-        ps += x;
-      }
-    }
-    l += pair_sum(ps);
+    l += ps;
     // O^T += V^T P^T over four 16-slot groups; four independent accumulators
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      bf16x8_t pb;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pb[e] = __bf16(acc[g >> 1][8 * (g & 1) + e]);
       const unsigned char* vrow = vc + 16 * g * Cfg::kRowBytes;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
         const uint2 lo = lds_read_tr16(vrow + voff[db]);
         const uint2 hi = lds_read_tr16(vrow + 8 * Cfg::kRowBytes + voff[db]);
-        o[db] = mfma32x32x16(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), pb, o[db]);
+        o[db] = mfma32x32x16(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), pb[g], o[db]);
       }
     }
   };
