@@ -251,21 +251,28 @@ void attn_fwd_bf16(Dims P, const uint16_t* __restrict__ q, const uint16_t* __res
     // and when the logits grow by more than about 64 - 6 in log2 units. Values up to
     // 2^64 are exact enough (relative rounding does not depend on magnitude) and keep
     // O and l far from overflow.
+    // The row sum adds the bf16-rounded probabilities, two per dot2 instruction:
+    // the same values the P V product uses.
     bf16x8_t pb[4];
     float ps;
     auto probs = [&]() {
-      ps = 0.0f;
 #pragma unroll
       for (int g = 0; g < 8; ++g) {
         const float bias = lwg[g] - m;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float x = fast_exp2(__builtin_fmaf(acc[g >> 2][(g & 3) * 4 + e], c2, bias));
-          pb[g >> 1][(g & 1) * 4 + e] = __bf16(x);
-          ps += x;
-        }
+        for (int e = 0; e < 4; ++e)
+          pb[g >> 1][(g & 1) * 4 + e] = __bf16(fast_exp2(__builtin_fmaf(acc[g >> 2][(g & 3) * 4 + e], c2, bias)));
       }
-      ps = pair_sum(ps);
+      const bf16x2_t ones = {__bf16(1.0f), __bf16(1.0f)};
+      float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        s0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2_t{pb[j][0], pb[j][1]}, ones, s0, false);
+        s1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2_t{pb[j][2], pb[j][3]}, ones, s1, false);
+        s0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2_t{pb[j][4], pb[j][5]}, ones, s0, false);
+        s1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2_t{pb[j][6], pb[j][7]}, ones, s1, false);
+      }
+      ps = pair_sum(s0 + s1);
     };
     probs();
     if (__builtin_amdgcn_ballot_w64(!(ps <= 1.8446744e19f)) != 0) {
