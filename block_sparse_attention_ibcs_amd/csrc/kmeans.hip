@@ -24,7 +24,23 @@
 namespace ab {
 namespace {
 
+// Separately rounded fp32 operations. HIP's __fmul_rn and __fadd_rn are plain
+// operators defined in its headers, where contraction is allowed, so once
+// inlined they can still be fused into an FMA; these helpers carry the
+// no-contraction setting of their own bodies instead.
+__device__ __forceinline__ float sub_rn(float a, float b) {
 #pragma clang fp contract(off)
+  return a - b;
+}
+__device__ __forceinline__ float sqr_acc_rn(float acc, float t) {
+#pragma clang fp contract(off)
+  const float t2 = t * t;
+  return acc + t2;
+}
+__device__ __forceinline__ float add_rn(float a, float b) {
+#pragma clang fp contract(off)
+  return a + b;
+}
 
 // Each thread keeps one query in VGPRs (bf16 pairs packed, unpacked at use); the
 // block also sits in LDS (its input type) for the centroid update.
@@ -122,8 +138,7 @@ __global__ __launch_bounds__(256) void kmeans_kernel(Dims P, const void* __restr
           const float m[4] = {m4.x, m4.y, m4.z, m4.w};
 #pragma unroll
           for (int cc = 0; cc < 4; ++cc) {
-            const float df = __fsub_rn(xk, m[cc]);
-            acc[cc] = __fadd_rn(acc[cc], __fmul_rn(df, df));
+            acc[cc] = sqr_acc_rn(acc[cc], sub_rn(xk, m[cc]));
           }
         }
         const int lim = min(4, Ci - cb);
@@ -176,7 +191,7 @@ __global__ __launch_bounds__(256) void kmeans_kernel(Dims P, const void* __restr
       if (cnt > 0) {
         const int st = cstart[c];
         float s = 0.0f;
-        for (int m = 0; m < cnt; ++m) s = __fadd_rn(s, xlds(list[st + m], k));
+        for (int m = 0; m < cnt; ++m) s = add_rn(s, xlds(list[st + m], k));
         mu_t[k * CP + c] = __fdiv_rn(s, float(cnt));
       }
     }

@@ -148,3 +148,17 @@ def test_bf16_rounding_matches_torch():
     x = np.concatenate([rng.standard_normal(10000).astype(np.float32) * 10, np.array([0.0, -0.0, 1.0, 3.0039062, 1e-40], dtype=np.float32)])
     ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
     np.testing.assert_array_equal(round_bf16(x), ref)
+
+
+@pytest.mark.parametrize("dim", [64, 128])
+def test_kmeans_rounds_multiply_and_add_separately(dim):
+    """On a block built so that one row's two distances are equal in exact arithmetic,
+    the oracle's assignment is the one of separately rounded multiplies and adds
+    (computed here term by term) and not the one of a fused multiply-add (computed
+    with exact rationals): the spec's rounding is what decides it."""
+    import kmeans_rounding_case as case
+
+    X, row, separate, fused = case.build(dim)
+    assert separate != fused
+    _, _, assign = kmeans_fp32(X, 2, 1)
+    assert int(assign[row]) == separate
