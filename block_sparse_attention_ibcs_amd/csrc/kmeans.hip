@@ -80,11 +80,10 @@ __global__ __launch_bounds__(256) void kmeans_kernel(Dims P, const void* __restr
   elem_t* X = reinterpret_cast<elem_t*>(smem);                                       // [Bq][D]
   float* mu_t = reinterpret_cast<float*>(smem + size_t(Bq) * D * sizeof(elem_t));    // [D][CP]
   int* asg = reinterpret_cast<int*>(mu_t + size_t(D) * CP);                          // [Bq]
-  int* list = asg + Bq;                                                              // [Bq]
-  int* cstart = list + Bq;                                                           // [C]
-  int* ccount = cstart + C;                                                          // [C]
-  float* pbest = reinterpret_cast<float*>(ccount + C);                               // [Bq] best of the upper half
+  float* pbest = reinterpret_cast<float*>(asg + Bq);                                 // [Bq] best of the upper half
   int* pidx = reinterpret_cast<int*>(pbest + Bq);                                    // [Bq]
+  int* ccount = pidx + Bq;                                                           // [C], padded to 16 bytes
+  uint8_t* list = reinterpret_cast<uint8_t*>(ccount + ((C + 3) & ~3));               // [C][Bq] member rows
 
   const elem_t* qsrc = reinterpret_cast<const elem_t*>(qv) + (size_t(bh) * P.N + row0) * D;
   {
@@ -165,33 +164,42 @@ __global__ __launch_bounds__(256) void kmeans_kernel(Dims P, const void* __restr
       asg[r_own] = bi;
     }
     __syncthreads();
-    // ---- member lists (ascending rows per cluster), one wave ----
-    if (wave == 0) {
-      int base = 0;
-      for (int c = 0; c < Ci; ++c) {
-        const int st = base;
-        for (int r0 = 0; r0 < n; r0 += 64) {
-          const int r = r0 + lane;
-          const bool pred = (r < n) && (asg[r] == c);
-          const uint64_t m = __ballot(pred);
-          if (pred) list[base + __popcll(m & ((uint64_t(1) << lane) - 1))] = r;
-          base += __popcll(m);
-        }
-        if (lane == 0) {
-          cstart[c] = st;
-          ccount[c] = base - st;
-        }
+    // ---- member lists (ascending rows per cluster); wave w builds clusters w, w + waves, ... ----
+    {
+      const int nwaves = nthr >> 6;
+      int a_lo = -1, a_hi = -1;  // assignments of rows lane and 64 + lane
+      if (lane < n) a_lo = asg[lane];
+      if (64 + lane < n) a_hi = asg[64 + lane];
+      for (int c = wave; c < Ci; c += nwaves) {
+        uint8_t* lc = list + c * Bq;
+        const uint64_t m_lo = __ballot(a_lo == c);
+        const uint64_t m_hi = __ballot(a_hi == c);
+        const uint64_t below = (uint64_t(1) << lane) - 1;
+        if (a_lo == c) lc[__popcll(m_lo & below)] = uint8_t(lane);
+        if (a_hi == c) lc[__popcll(m_lo) + __popcll(m_hi & below)] = uint8_t(64 + lane);
+        if (lane == 0) ccount[c] = __popcll(m_lo) + __popcll(m_hi);
       }
     }
     __syncthreads();
     // ---- update: members summed in ascending row order, one correctly rounded division ----
+    // (c, k) with k fastest: a wave shares c, so the member loop is uniform; member rows
+    // are fetched eight at a time ahead of the in-order adds
     for (int p = tid; p < Ci * D; p += nthr) {
       const int c = p / D, k = p % D;
       const int cnt = ccount[c];
       if (cnt > 0) {
-        const int st = cstart[c];
+        const uint8_t* lc = list + c * Bq;
         float s = 0.0f;
-        for (int m = 0; m < cnt; ++m) s = add_rn(s, xlds(list[st + m], k));
+        int m = 0;
+        for (; m + 8 <= cnt; m += 8) {
+          const uint2 rr = *reinterpret_cast<const uint2*>(lc + m);
+          float v[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) v[u] = xlds(int(((u < 4 ? rr.x : rr.y) >> (8 * (u & 3))) & 0xFFu), k);
+#pragma unroll
+          for (int u = 0; u < 8; ++u) s = add_rn(s, v[u]);
+        }
+        for (; m < cnt; ++m) s = add_rn(s, xlds(lc[m], k));
         mu_t[k * CP + c] = __fdiv_rn(s, float(cnt));
       }
     }
@@ -216,7 +224,8 @@ template <bool BF16, int D>
 hipError_t launch(const Dims& P, const void* q, float* cent, uint16_t* cb, int32_t* sz, uint8_t* as,
                   hipStream_t s) {
   const int CP = (P.C + 7) & ~7;
-  const size_t lds = size_t(P.Bq) * D * (BF16 ? 2 : 4) + size_t(D) * CP * 4 + size_t(P.Bq) * 16 + size_t(P.C) * 8;
+  const size_t lds = size_t(P.Bq) * D * (BF16 ? 2 : 4) + size_t(D) * CP * 4 + size_t(P.Bq) * 12 +
+                    size_t((P.C + 3) & ~3) * 4 + size_t(P.C) * P.Bq;
   auto kern = kmeans_kernel<BF16, D>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
