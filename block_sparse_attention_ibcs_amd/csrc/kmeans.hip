@@ -183,7 +183,8 @@ __global__ __launch_bounds__(256) void kmeans_kernel(Dims P, const void* __restr
     __syncthreads();
     // ---- update: members summed in ascending row order, one correctly rounded division ----
     // (c, k) with k fastest: a wave shares c, so the member loop is uniform; member rows
-    // are fetched eight at a time ahead of the in-order adds
+    // are fetched eight at a time ahead of the in-order adds, and the next eight list
+    // entries while those rows are read
     for (int p = tid; p < Ci * D; p += nthr) {
       const int c = p / D, k = p % D;
       const int cnt = ccount[c];
@@ -191,11 +192,14 @@ __global__ __launch_bounds__(256) void kmeans_kernel(Dims P, const void* __restr
         const uint8_t* lc = list + c * Bq;
         float s = 0.0f;
         int m = 0;
+        uint2 rr = *reinterpret_cast<const uint2*>(lc);
         for (; m + 8 <= cnt; m += 8) {
-          const uint2 rr = *reinterpret_cast<const uint2*>(lc + m);
           float v[8];
 #pragma unroll
           for (int u = 0; u < 8; ++u) v[u] = xlds(int(((u < 4 ? rr.x : rr.y) >> (8 * (u & 3))) & 0xFFu), k);
+          // next batch's member rows, in flight with this batch's reads (the list
+          // region of a cluster holds Bq entries, so m + 8 stays inside it)
+          rr = *reinterpret_cast<const uint2*>(lc + min(m + 8, Bq - 8));
 #pragma unroll
           for (int u = 0; u < 8; ++u) s = add_rn(s, v[u]);
         }
