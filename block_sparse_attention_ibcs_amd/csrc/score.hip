@@ -50,12 +50,11 @@ template <int BK>
 __device__ __forceinline__ void lse_block(const f32x16_t& acc, LseState& st, float c2, int kb, int key_end,
                                           int half, bool row_ok, float* ell_row, int C, int nkb) {
   float ev[16];
-  float s_own = 0.0f;
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    ev[e] = fast_exp2(__builtin_fmaf(acc[e], c2, -st.mref));
-    s_own += ev[e];
-  }
+  for (int e = 0; e < 16; ++e) ev[e] = fast_exp2(__builtin_fmaf(acc[e], c2, -st.mref));
+  float s_own = ev[0];
+#pragma unroll
+  for (int e = 1; e < 16; ++e) s_own += ev[e];
   float s_pair = pair_sum(s_own);
   // rebase when the reference is unset (first block) or a sum would pass 2^64
   if (__builtin_amdgcn_ballot_w64(!(s_pair < 1.8446744e19f)) != 0) {
@@ -67,12 +66,11 @@ __device__ __forceinline__ void lse_block(const f32x16_t& acc, LseState& st, flo
     st.tot *= f;
     st.sub *= f;
     st.mref = nref;
-    s_own = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      ev[e] = fast_exp2(__builtin_fmaf(acc[e], c2, -st.mref));
-      s_own += ev[e];
-    }
+    for (int e = 0; e < 16; ++e) ev[e] = fast_exp2(__builtin_fmaf(acc[e], c2, -st.mref));
+    s_own = ev[0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) s_own += ev[e];
     s_pair = pair_sum(s_own);
   }
   st.tot += s_pair;
@@ -104,7 +102,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 4)))
 void score_lse_bf16(Dims P, int split_keys, int splits, int row_tiles, const uint16_t* __restrict__ keys,
                     const uint16_t* __restrict__ cent, float* __restrict__ ell, float* __restrict__ lpart) {
   using Cfg = LseCfg<D>;
-  constexpr uint32_t kOOB = 0x80000000u;
   __shared__ __align__(16) unsigned char kb0[Cfg::kTileBytes];
   __shared__ __align__(16) unsigned char kb1[Cfg::kTileBytes];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -140,16 +137,21 @@ void score_lse_bf16(Dims P, int split_keys, int splits, int row_tiles, const uin
   }
   const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(keys + size_t(bh) * N * D), (short)0, N * Cfg::kRowBytes, 0x00020000);
-  auto issue_tile = [&](int t, unsigned char* dst) {
+  // Per-lane constant part of each gather load's byte offset (key row in the tile,
+  // permuted chunk). Keys past the split end but below N are gathered too and masked
+  // in the math; rows at or past N read zeros through the buffer range check.
+  uint32_t gofs[Cfg::kLoadsPerWave];
 #pragma unroll
-    for (int j = 0; j < Cfg::kLoadsPerWave; ++j) {
-      const int ld = wave * Cfg::kLoadsPerWave + j;
-      const int krow = ld * Cfg::kKeysPerLoad + lane / Cfg::kChunks;
-      const int key = key_begin + t * kTileKeys + krow;
-      const int pos = lane % Cfg::kChunks;
-      const uint32_t off = key < key_end ? uint32_t(key) * Cfg::kRowBytes + ((pos ^ kfrag_swz<D>(krow)) << 4) : kOOB;
-      buffer_load_lds16(rk, dst + ld * 1024, off);
-    }
+  for (int j = 0; j < Cfg::kLoadsPerWave; ++j) {
+    const int krow = (wave * Cfg::kLoadsPerWave + j) * Cfg::kKeysPerLoad + lane / Cfg::kChunks;
+    const int pos = lane % Cfg::kChunks;
+    gofs[j] = uint32_t(krow * Cfg::kRowBytes + ((pos ^ kfrag_swz<D>(krow)) << 4));
+  }
+  auto issue_tile = [&](int t, unsigned char* dst) {
+    const uint32_t base = uint32_t(key_begin + t * kTileKeys) * Cfg::kRowBytes;
+#pragma unroll
+    for (int j = 0; j < Cfg::kLoadsPerWave; ++j)
+      buffer_load_lds16(rk, dst + (wave * Cfg::kLoadsPerWave + j) * 1024, base + gofs[j]);
   };
   int koff[D / 16];
 #pragma unroll
