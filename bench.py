@@ -44,6 +44,9 @@ def parse_args():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="wall time budget of the CPU oracle sample")
+    ap.add_argument("--sweep", action="store_true",
+                    help="gather-cost sweep on the 75600-token, 40-head shape: density {1, .25, .10, .05} x k_block "
+                         "{16, 32, 64, 128}; one JSON line per point instead of the headline line")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one device copy of this many MiB before timing (reference kernel for HBM counters)")
     return ap.parse_args()
@@ -70,6 +73,111 @@ def read_traffic(workload):
         return float(vals["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def attention_work(w, nqb, nkb, idx, cnt):
+    """Actually computed attention work of one launch, 4*d*sum over query rows of the kept
+    real keys (the ragged tail block counts its real keys only), and the realised density."""
+    import torch
+
+    tail = w.N - (nkb - 1) * w.k_block
+    counts = cnt.to(torch.int64)
+    last_kept = torch.zeros_like(counts)
+    nz = counts > 0
+    last_idx = torch.gather(idx.to(torch.int64), 3, (counts.clamp(min=1) - 1).unsqueeze(-1)).squeeze(-1)
+    last_kept[nz & (last_idx == nkb - 1)] = 1
+    keys = counts * w.k_block - last_kept * (w.k_block - tail)
+    rows_per_block = torch.full((nqb,), w.q_block, dtype=torch.int64, device=idx.device)
+    rows_per_block[-1] = w.N - (nqb - 1) * w.q_block
+    flops = float((4 * w.d * (keys * rows_per_block.view(1, 1, -1)).sum()).item())
+    return flops, float(counts.sum().item()) / (w.B * w.H * nqb * nkb)
+
+
+SWEEP_DENSITIES = (1.0, 0.25, 0.10, 0.05)
+SWEEP_K_BLOCKS = (16, 32, 64, 128)
+
+
+def run_sweep(args):
+    """Gather-cost sweep: the scorer once per key sub-block size, then sampler and attention
+    at every density, each stage timed with HIP events on its stream over args.steps
+    launches. Density 1 keeps every sub-block, so its attention time is set against the
+    dense bf16 roofline of the same shape."""
+    import numpy as np
+    import torch
+
+    import block_sparse_attention_ibcs_amd as ab
+    import workloads
+
+    w0 = workloads.get("wan14b")
+    q, k, v = workloads.generate(w0, seed=0)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = (torch.from_numpy(x).to(torch.bfloat16).to(dev) for x in (q, k, v))
+    del q, k, v
+    stream = torch.cuda.current_stream()
+    dense = w0.dense_flops()
+    dense_roof_ms = dense / (PEAK_BF16_TFLOPS * 1e12) * 1e3
+
+    def timed(fn, reps):
+        evs = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            evs.append((a, b))
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    for bk in SWEEP_K_BLOCKS:
+        w = w0.with_(k_block=bk)
+        desc = ab.Desc.for_tensor(qd, w.q_block, bk, w.n_clusters, w.kmeans_iters)
+        nqb, nkb = desc.nqb, desc.nkb
+        rows = (w.B, w.H, nqb)
+        ws = ab.alloc_workspace(desc, dev)
+        scores = torch.empty(rows + (nkb,), dtype=torch.float32, device=dev)
+        idx = torch.empty(rows + (nkb,), dtype=torch.int32, device=dev)
+        wts = torch.empty(rows + (nkb,), dtype=torch.float32, device=dev)
+        cnt = torch.empty(rows, dtype=torch.int32, device=dev)
+        out = torch.empty_like(qd)
+        lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+        score_fn = lambda: ab.ab_score(desc, qd, kd, scores=scores, workspace=ws)  # noqa: E731
+        for _ in range(args.warmup):
+            score_fn()
+        score_ms = timed(score_fn, args.steps)
+        for rho in SWEEP_DENSITIES:
+            sample_fn = lambda: ab.ab_sample(desc, scores, rho, args.seed, idx=idx, weights=wts,  # noqa: E731
+                                             counts=cnt, want_mask=False)
+            attn_fn = lambda: ab.ab_attn_fwd(desc, qd, kd, vd, idx, wts, cnt, out=out, lse=lse)  # noqa: E731
+            sample_fn()
+            attn_fn()
+            torch.cuda.synchronize()
+            flops, realised = attention_work(w, nqb, nkb, idx, cnt)
+            for _ in range(args.warmup):
+                attn_fn()
+            sample_ms = timed(sample_fn, args.steps)
+            attn_ms = timed(attn_fn, args.steps)
+            achieved = flops / (attn_ms / 1e3) / 1e12
+            layer_ms = score_ms + sample_ms + attn_ms
+            print(json.dumps({
+                "sweep": "gather-cost",
+                "workload": f"wan14b shape: B={w.B} H={w.H} N={w.N} d={w.d} Bq={w.q_block} C={w.n_clusters}",
+                "k_block": bk,
+                "density": rho,
+                "realised_density": realised,
+                "score_ms": score_ms,
+                "sample_ms": sample_ms,
+                "attn_ms": attn_ms,
+                "layer_ms": layer_ms,
+                "attn_actual_tflops": achieved,
+                "attn_mfma_frac": achieved / PEAK_BF16_TFLOPS,
+                "attn_flops": flops,
+                "attn_dense_equivalent_tflops": dense / (attn_ms / 1e3) / 1e12,
+                "layer_dense_equivalent_tflops": dense / (layer_ms / 1e3) / 1e12,
+                "dense_roofline_ms": dense_roof_ms,
+                "steps": args.steps,
+            }), flush=True)
+        del ws, scores, idx, wts, cnt, out, lse
+        torch.cuda.empty_cache()
 
 
 def cpu_baseline(w, q, k, v, density, seed, budget_s):
@@ -128,6 +236,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     ab.load_library()  # fails loudly if the HIP library is not built
+    if args.sweep:
+        run_sweep(args)
+        return
     w = workloads.get(args.workload)
     if args.k_block:
         w = w.with_(k_block=args.k_block)
@@ -192,19 +303,8 @@ def main():
     torch.cuda.synchronize()
     stage_ms = {k_: float(np.mean([a.elapsed_time(b) for a, b in v_])) for k_, v_ in ev.items()}
 
-    # actually computed attention work of one launch: 4*d*sum over query rows of the kept keys
-    tail = w.N - (nkb - 1) * w.k_block
-    counts = cnt.to(torch.int64)
-    last_kept = torch.zeros_like(counts)
-    nz = counts > 0
-    last_idx = torch.gather(idx.to(torch.int64), 3, (counts.clamp(min=1) - 1).unsqueeze(-1)).squeeze(-1)
-    last_kept[nz & (last_idx == nkb - 1)] = 1
-    keys = counts * w.k_block - last_kept * (w.k_block - tail)
-    rows_per_block = torch.full((nqb,), w.q_block, dtype=torch.int64, device=dev)
-    rows_per_block[-1] = w.N - (nqb - 1) * w.q_block
-    actual_flops = float((4 * w.d * (keys * rows_per_block.view(1, 1, -1)).sum()).item())
+    actual_flops, realised = attention_work(w, nqb, nkb, idx, cnt)
     dense = w.dense_flops()
-    realised = float(counts.sum().item()) / (w.B * w.H * nqb * nkb)
 
     attn_s = stage_ms["attn"] / 1e3
     achieved = actual_flops / attn_s / 1e12
