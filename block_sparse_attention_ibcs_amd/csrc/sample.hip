@@ -17,8 +17,9 @@
 // its own four Philox blocks, computes thresholds with one reciprocal per row
 // and an exact integer fix-up, and a wave prefix sum over the lanes' popcounts
 // places the kept indices in ascending order.
-// Longer rows: one workgroup per row, the capped set in an LDS bitset, scores
-// re-read on every pass.
+// Rows of up to 16384 sub-blocks: the same scheme with one 256-thread workgroup per
+// row and workgroup reductions. Longer rows: one workgroup per row, the capped set in
+// an LDS bitset, scores re-read on every pass.
 #include "ab_internal.h"
 
 namespace ab {
@@ -364,6 +365,157 @@ __global__ __launch_bounds__(256) void sample_wave_kernel(Dims P, int K, int row
   if (lane == 0) counts[row] = base;
 }
 
+// Rows of 4097..16384 sub-blocks: one 256-thread workgroup per row, thread t holds
+// the quantized scores of sub-blocks [4096c + 16t, 4096c + 16t + 16) of every
+// 4096-wide chunk c in VGPRs; water-filling sums are workgroup reductions and the
+// compaction is a workgroup prefix sum per chunk.
+constexpr int kBlockChunk = kThreads * kLaneElems;
+
+template <int NCH>
+__global__ __launch_bounds__(kThreads) void sample_block_kernel(Dims P, int K, uint32_t seed_lo, uint32_t seed_hi,
+                                                                const float* __restrict__ scores,
+                                                                int32_t* __restrict__ idx,
+                                                                float* __restrict__ weights,
+                                                                int32_t* __restrict__ counts,
+                                                                uint32_t* __restrict__ mask) {
+  __shared__ uint64_t red64[4];
+  __shared__ int red32[4];
+  __shared__ int wtot[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int row = blockIdx.x;  // (b*H + h)*nqb + i
+  const int nkb = P.nkb;
+  const int i = row % P.nqb;
+  const int bh = row / P.nqb;
+  const int h = bh % P.H, b = bh / P.H;
+  const float* s = scores + size_t(row) * nkb;
+  const bool vec_ok = (nkb & 3) == 0;
+
+  uint32_t w[NCH][kLaneElems];
+  uint32_t valid[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int j0 = c * kBlockChunk + tid * kLaneElems;
+    const int nv = min(kLaneElems, max(0, nkb - j0));
+    valid[c] = (1u << nv) - 1u;  // nv <= 16
+    if (vec_ok && nv == kLaneElems) {
+      const float4* s4 = reinterpret_cast<const float4*>(s + j0);
+#pragma unroll
+      for (int q = 0; q < kLaneElems / 4; ++q) {
+        const float4 v = s4[q];
+        w[c][4 * q + 0] = quantize(v.x);
+        w[c][4 * q + 1] = quantize(v.y);
+        w[c][4 * q + 2] = quantize(v.z);
+        w[c][4 * q + 3] = quantize(v.w);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < kLaneElems; ++e) w[c][e] = (e < nv) ? quantize(s[j0 + e]) : 0u;
+    }
+  }
+
+  // ---- integer water-filling ----
+  uint32_t cap[NCH];
+  uint64_t room = 0, S = 1;
+  if (K >= nkb) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) cap[c] = valid[c];
+  } else {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) cap[c] = 0u;
+    int m = 0;
+    for (;;) {
+      uint32_t part = 0;  // at most 64 values below 2^25
+#pragma unroll
+      for (int c = 0; c < NCH; ++c)
+#pragma unroll
+        for (int e = 0; e < kLaneElems; ++e) part += ((cap[c] >> e) & 1u) ? 0u : w[c][e];
+      S = block_sum<uint64_t>(uint64_t(part), red64);
+      room = uint64_t(K - m);
+      int nnew = 0;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+#pragma unroll
+        for (int e = 0; e < kLaneElems; ++e) {
+          const bool un = ((valid[c] & ~cap[c]) >> e) & 1u;
+          if (un && room * uint64_t(w[c][e]) >= S) {
+            cap[c] |= 1u << e;
+            ++nnew;
+          }
+        }
+      }
+      nnew = block_sum<int>(nnew, red32);
+      if (nnew == 0) break;
+      m += nnew;
+    }
+  }
+
+  // ---- draw: thresholds replace the weights in place ----
+  const double rS = 1.0 / double(S);
+  uint32_t keep[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    keep[c] = 0u;
+    const int g0 = (c * kBlockChunk + tid * kLaneElems) >> 2;
+#pragma unroll
+    for (int g = 0; g < kLaneElems / 4; ++g) {
+      if (!((valid[c] >> (4 * g)) & 0xFu)) continue;
+      const uint4 r = philox4x32_10(uint32_t(g0 + g), uint32_t(i), uint32_t(h), uint32_t(b), seed_lo, seed_hi);
+      const uint32_t rr[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const int e = 4 * g + e4;
+        uint32_t t = kOne;
+        if (!((cap[c] >> e) & 1u)) {
+          const uint32_t q = floor_div_est(room * uint64_t(w[c][e]) * uint64_t(kOne), S, rS);
+          t = q > 0u ? q : 1u;
+        }
+        w[c][e] = t;
+        if (((valid[c] >> e) & 1u) && (rr[e4] >> 8) < t) keep[c] |= 1u << e;
+      }
+    }
+  }
+
+  // ---- compaction in ascending sub-block order: chunk, then thread, then element ----
+  const size_t out0 = size_t(row) * nkb;
+  const int words = ceil_div(nkb, 32);
+  int base = 0;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int pc = __popc(keep[c]);
+    int incl = pc;
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += y;
+    }
+    __syncthreads();  // wtot of the previous chunk is consumed
+    if (lane == 63) wtot[wave] = incl;
+    __syncthreads();
+    int woff = 0, tot = 0;
+#pragma unroll
+    for (int wv = 0; wv < kThreads / 64; ++wv) {
+      woff += wv < wave ? wtot[wv] : 0;
+      tot += wtot[wv];
+    }
+    int pos = base + woff + incl - pc;
+    const int j0 = c * kBlockChunk + tid * kLaneElems;
+#pragma unroll
+    for (int e = 0; e < kLaneElems; ++e) {
+      if ((keep[c] >> e) & 1u) {
+        idx[out0 + pos] = j0 + e;
+        weights[out0 + pos] = __fdiv_rn(16777216.0f, float(w[c][e]));
+        ++pos;
+      }
+    }
+    base += tot;
+    if (mask) {
+      const uint32_t hi = __shfl_down(keep[c], 1, 64);
+      const int wd = (c * kBlockChunk) / 32 + tid / 2;
+      if (!(tid & 1) && wd < words) mask[size_t(row) * words + wd] = keep[c] | (hi << 16);
+    }
+  }
+  if (tid == 0) counts[row] = base;
+}
+
 }  // namespace
 
 hipError_t launch_sample(const Dims& P, const float* scores, int K, uint64_t seed, int32_t* idx, float* weights,
@@ -378,9 +530,17 @@ hipError_t launch_sample(const Dims& P, const float* scores, int K, uint64_t see
     case 3: hipLaunchKernelGGL(sample_wave_kernel<3>, grid, block, 0, s, P, K, rows, lo, hi, scores, idx, weights, counts, mask); break;
     case 4: hipLaunchKernelGGL(sample_wave_kernel<4>, grid, block, 0, s, P, K, rows, lo, hi, scores, idx, weights, counts, mask); break;
     default: {
-      const size_t lds = size_t(ceil_div(P.nkb, 32)) * 4;
-      hipLaunchKernelGGL(sample_kernel, dim3(rows), dim3(kThreads), lds, s, P, K, lo, hi, scores, idx, weights,
-                         counts, mask);
+      const int nchb = ceil_div(P.nkb, kBlockChunk);
+      const dim3 g(rows), t(kThreads);
+      switch (nchb) {
+        case 2: hipLaunchKernelGGL(sample_block_kernel<2>, g, t, 0, s, P, K, lo, hi, scores, idx, weights, counts, mask); break;
+        case 3: hipLaunchKernelGGL(sample_block_kernel<3>, g, t, 0, s, P, K, lo, hi, scores, idx, weights, counts, mask); break;
+        case 4: hipLaunchKernelGGL(sample_block_kernel<4>, g, t, 0, s, P, K, lo, hi, scores, idx, weights, counts, mask); break;
+        default: {
+          const size_t lds = size_t(ceil_div(P.nkb, 32)) * 4;
+          hipLaunchKernelGGL(sample_kernel, g, t, lds, s, P, K, lo, hi, scores, idx, weights, counts, mask);
+        }
+      }
     }
   }
   return hipGetLastError();

@@ -359,13 +359,16 @@ def test_edge_shapes(N, H, d, Bq, Bk, C, T, density):
 
 
 @pytest.mark.parametrize("nkb,density", [(37, 0.3), (1024, 0.1), (1000, 1.0), (1500, 0.02), (2363, 0.1),
-                                         (4096, 0.5), (4100, 0.1), (9000, 0.05)])
+                                         (4096, 0.5), (4100, 0.1), (4725, 0.08), (7425, 1.0), (9000, 0.05),
+                                         (16384, 0.1), (20000, 0.02)])
 def test_sampler_rows_any_length(nkb, density):
     """The sampler alone on synthetic score rows: short rows, each register-resident
-    row length class, and rows long enough for the LDS-bitset path; peaked rows force
-    several water-filling passes; zero, negative, NaN, sub-2^-24 and >= 1 scores."""
+    row length class (one wave per row up to 4096 sub-blocks, one workgroup per row up
+    to 16384), and rows long enough for the LDS-bitset path; peaked rows force several
+    water-filling passes; zero, negative, NaN, sub-2^-24 and >= 1 scores."""
     _gpu()
-    Bk, Bq, H = 16, 128, 2
+    Bk, Bq = 16, 128
+    H = 1 if nkb > 16384 else 2
     N = nkb * Bk - 3  # ragged last sub-block
     desc = ab.Desc(1, H, N, 128, ab.AB_BF16, Bq, Bk, 8)
     assert desc.nkb == nkb
