@@ -181,7 +181,8 @@ def run_sweep(args):
 
 
 def cpu_baseline(w, q, k, v, density, seed, budget_s):
-    """Time the oracle (IBCS + SIP + weighted attention) on query blocks of head 0 for about budget_s seconds."""
+    """Time the oracle (IBCS + SIP + weighted attention) on query blocks for about budget_s seconds:
+    a seeded spread of the blocks of head 0, then of head 1, and so on."""
     import numpy as np
 
     import oracle
@@ -196,16 +197,16 @@ def cpu_baseline(w, q, k, v, density, seed, budget_s):
     except Exception:
         pass
     p = oracle.Params(w.q_block, w.k_block, w.n_clusters, w.kmeans_iters, density, bf16=w.dtype == "bf16")
-    # a spread of query blocks of head 0
-    order = np.random.default_rng(1).permutation(w.nqb)
+    order = [(0, h, int(i)) for h in range(w.B * w.H) for i in np.random.default_rng(1 + h).permutation(w.nqb)]
     t0 = time.perf_counter()
     done = []
-    for i in order:
-        oracle.run_blocks(q, k, v, p, seed, [(0, 0, int(i))])
-        done.append(int(i))
+    for (b, h, i) in order:
+        oracle.run_blocks(q, k, v, p, seed, [(h // w.H, h % w.H, i)])
+        done.append(i)
         if time.perf_counter() - t0 >= budget_s and len(done) >= 2:
             break
     dt = time.perf_counter() - t0
+    heads = len({bh for (_, bh, _) in order[:len(done)]})
     rows = sum(min(w.q_block, w.N - i * w.q_block) for i in done)
     dense_flops = 4.0 * rows * w.N * w.d
     return {
@@ -213,7 +214,7 @@ def cpu_baseline(w, q, k, v, density, seed, budget_s):
         "unit": "TFLOP/s (dense-equivalent)",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"{len(done)} query blocks ({rows} query rows) of head 0 through IBCS k-means, block scores, "
+        "sample": f"{len(done)} query blocks ({rows} query rows) of {heads} head(s) through IBCS k-means, block scores, "
                   f"SIP draw and weighted attention in float64/numpy; {dt:.1f} s wall "
                   f"({dt / len(done) * w.H * w.nqb:.0f} s extrapolated per layer)",
         "ms_per_layer_extrapolated": dt / len(done) * w.H * w.nqb * 1e3,
