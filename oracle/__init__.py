@@ -24,6 +24,7 @@ Pins (what fixes each function against something other than itself) live in
 from .philox import philox4x32_10
 from .ibcs import kmeans_fp32, block_scores, round_bf16
 from .sip import quantize_scores, budget, inclusion_thresholds, sample_rows, SIP_ONE
+from .topk import topk_rows
 from .attention import dense_attention, sparse_ht_attention
 from .pipeline import Params, run_blocks
 
@@ -36,6 +37,7 @@ __all__ = [
     "budget",
     "inclusion_thresholds",
     "sample_rows",
+    "topk_rows",
     "SIP_ONE",
     "dense_attention",
     "sparse_ht_attention",
