@@ -90,6 +90,16 @@ int32_t make_dims(const ab_desc* d, ab::Dims* P) {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
+// K = clamp(floor(density * NKB + 0.5), 1, NKB), two separately rounded fp64 operations
+int budget_blocks(double density, int nkb) {
+  volatile double prod = density * double(nkb);
+  const double t = prod + 0.5;
+  long long K = static_cast<long long>(std::floor(t));
+  if (K < 1) K = 1;
+  if (K > nkb) K = nkb;
+  return int(K);
+}
+
 }  // namespace
 
 extern "C" {
@@ -170,16 +180,28 @@ int32_t ab_sample(const ab_desc* desc, const float* scores, double density, uint
   if (rc) return rc;
   if (!scores || !idx || !weights || !counts) return fail(AB_ERR_NULL, "scores, idx, weights and counts must be non-NULL");
   if (!(density > 0.0 && density <= 1.0)) return fail(AB_ERR_DENSITY, "density %g not in (0, 1]", density);
-  // K = clamp(floor(density * NKB + 0.5), 1, NKB), two separately rounded fp64 operations
-  volatile double prod = density * double(P.nkb);
-  const double t = prod + 0.5;
-  long long K = static_cast<long long>(std::floor(t));
-  if (K < 1) K = 1;
-  if (K > P.nkb) K = P.nkb;
+  const int K = budget_blocks(density, P.nkb);
   if ((rc = check_device())) return rc;
-  hipError_t e = ab::launch_sample(P, scores, int(K), seed, idx, weights, counts, mask_bits,
+  hipError_t e = ab::launch_sample(P, scores, K, seed, idx, weights, counts, mask_bits,
                                    static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "sampler launch");
+  return AB_OK;
+}
+
+int32_t ab_sample_topk(const ab_desc* desc, const float* scores, double density, int32_t* idx, float* weights,
+                       int32_t* counts, uint32_t* mask_bits, void* stream) {
+  g_err[0] = 0;
+  ab::Dims P;
+  int32_t rc = make_dims(desc, &P);
+  if (rc) return rc;
+  if (!scores || !idx || !weights || !counts) return fail(AB_ERR_NULL, "scores, idx, weights and counts must be non-NULL");
+  if (!(density > 0.0 && density <= 1.0)) return fail(AB_ERR_DENSITY, "density %g not in (0, 1]", density);
+  if (P.nkb > ab::kTopkMaxNkb)
+    return fail(AB_ERR_SHAPE, "top-K truncation takes rows of at most %d sub-blocks (got %d)", ab::kTopkMaxNkb, P.nkb);
+  const int K = budget_blocks(density, P.nkb);
+  if ((rc = check_device())) return rc;
+  hipError_t e = ab::launch_topk(P, scores, K, idx, weights, counts, mask_bits, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "top-K launch");
   return AB_OK;
 }
 

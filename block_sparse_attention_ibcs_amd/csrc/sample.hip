@@ -516,6 +516,142 @@ __global__ __launch_bounds__(kThreads) void sample_block_kernel(Dims P, int K, u
   if (tid == 0) counts[row] = base;
 }
 
+// Exclusive prefix sum of v over the workgroup in thread order; total receives the sum.
+__device__ __forceinline__ int block_excl_scan(int v, int* wtot, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = v;
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += y;
+  }
+  __syncthreads();  // wtot of a previous scan is consumed
+  if (lane == 63) wtot[wave] = incl;
+  __syncthreads();
+  int woff = 0;
+  total = 0;
+#pragma unroll
+  for (int wv = 0; wv < kThreads / 64; ++wv) {
+    woff += wv < wave ? wtot[wv] : 0;
+    total += wtot[wv];
+  }
+  return woff + incl - v;
+}
+
+// Top-K truncation: one 256-thread workgroup per row, the quantized scores in VGPRs
+// as in sample_block_kernel. The cut value theta is the largest w with at least K
+// blocks at or above it (binary search over [1, 2^24], one workgroup count per
+// step); blocks above theta are kept, and of those equal to theta the lowest
+// K - #(w > theta) indices, found with a workgroup prefix count in index order.
+template <int NCH>
+__global__ __launch_bounds__(kThreads) void topk_block_kernel(Dims P, int K, const float* __restrict__ scores,
+                                                              int32_t* __restrict__ idx,
+                                                              float* __restrict__ weights,
+                                                              int32_t* __restrict__ counts,
+                                                              uint32_t* __restrict__ mask) {
+  __shared__ int red32[4];
+  __shared__ int wtot[4];
+  const int tid = threadIdx.x;
+  const int row = blockIdx.x;
+  const int nkb = P.nkb;
+  const float* s = scores + size_t(row) * nkb;
+  const bool vec_ok = (nkb & 3) == 0;
+
+  uint32_t w[NCH][kLaneElems];
+  uint32_t valid[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int j0 = c * kBlockChunk + tid * kLaneElems;
+    const int nv = min(kLaneElems, max(0, nkb - j0));
+    valid[c] = (1u << nv) - 1u;  // nv <= 16
+    if (vec_ok && nv == kLaneElems) {
+      const float4* s4 = reinterpret_cast<const float4*>(s + j0);
+#pragma unroll
+      for (int q = 0; q < kLaneElems / 4; ++q) {
+        const float4 v = s4[q];
+        w[c][4 * q + 0] = quantize(v.x);
+        w[c][4 * q + 1] = quantize(v.y);
+        w[c][4 * q + 2] = quantize(v.z);
+        w[c][4 * q + 3] = quantize(v.w);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < kLaneElems; ++e) w[c][e] = (e < nv) ? quantize(s[j0 + e]) : 0u;
+    }
+  }
+  auto count_ge = [&](uint32_t th) {
+    int n = 0;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+#pragma unroll
+      for (int e = 0; e < kLaneElems; ++e) n += (((valid[c] >> e) & 1u) && w[c][e] >= th) ? 1 : 0;
+    return block_sum<int>(n, red32);
+  };
+
+  uint32_t keep[NCH];
+  if (K >= nkb) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) keep[c] = valid[c];
+  } else {
+    uint32_t lo = 1u, hi = kOne + 1u;  // count_ge(lo) = nkb >= K, count_ge(hi) = 0 < K
+    while (hi - lo > 1u) {
+      const uint32_t mid = lo + (hi - lo) / 2u;
+      if (count_ge(mid) >= K) lo = mid; else hi = mid;
+    }
+    const uint32_t theta = lo;
+    const int need = K - count_ge(theta + 1u);  // blocks equal to theta to keep, lowest index first
+    int tie_base = 0;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      uint32_t above = 0u, tie = 0u;
+#pragma unroll
+      for (int e = 0; e < kLaneElems; ++e) {
+        if ((valid[c] >> e) & 1u) {
+          above |= (w[c][e] > theta ? 1u : 0u) << e;
+          tie |= (w[c][e] == theta ? 1u : 0u) << e;
+        }
+      }
+      int tot = 0;
+      int rank = tie_base + block_excl_scan(__popc(tie), wtot, tot);
+      uint32_t kt = 0u;
+#pragma unroll
+      for (int e = 0; e < kLaneElems; ++e) {
+        if ((tie >> e) & 1u) {
+          if (rank < need) kt |= 1u << e;
+          ++rank;
+        }
+      }
+      keep[c] = above | kt;
+      tie_base += tot;
+    }
+  }
+
+  // ---- compaction in ascending sub-block order, weight 1 ----
+  const size_t out0 = size_t(row) * nkb;
+  const int words = ceil_div(nkb, 32);
+  int base = 0;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    int tot = 0;
+    int pos = base + block_excl_scan(__popc(keep[c]), wtot, tot);
+    const int j0 = c * kBlockChunk + tid * kLaneElems;
+#pragma unroll
+    for (int e = 0; e < kLaneElems; ++e) {
+      if ((keep[c] >> e) & 1u) {
+        idx[out0 + pos] = j0 + e;
+        weights[out0 + pos] = 1.0f;
+        ++pos;
+      }
+    }
+    base += tot;
+    if (mask) {
+      const uint32_t hi16 = __shfl_down(keep[c], 1, 64);
+      const int wd = (c * kBlockChunk) / 32 + tid / 2;
+      if (!(tid & 1) && wd < words) mask[size_t(row) * words + wd] = keep[c] | (hi16 << 16);
+    }
+  }
+  if (tid == 0) counts[row] = base;
+}
+
 }  // namespace
 
 hipError_t launch_sample(const Dims& P, const float* scores, int K, uint64_t seed, int32_t* idx, float* weights,
@@ -542,6 +678,18 @@ hipError_t launch_sample(const Dims& P, const float* scores, int K, uint64_t see
         }
       }
     }
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_topk(const Dims& P, const float* scores, int K, int32_t* idx, float* weights, int32_t* counts,
+                       uint32_t* mask, hipStream_t s) {
+  const dim3 g(P.B * P.H * P.nqb), t(kThreads);
+  switch (ceil_div(P.nkb, kBlockChunk)) {
+    case 1: hipLaunchKernelGGL(topk_block_kernel<1>, g, t, 0, s, P, K, scores, idx, weights, counts, mask); break;
+    case 2: hipLaunchKernelGGL(topk_block_kernel<2>, g, t, 0, s, P, K, scores, idx, weights, counts, mask); break;
+    case 3: hipLaunchKernelGGL(topk_block_kernel<3>, g, t, 0, s, P, K, scores, idx, weights, counts, mask); break;
+    default: hipLaunchKernelGGL(topk_block_kernel<4>, g, t, 0, s, P, K, scores, idx, weights, counts, mask);
   }
   return hipGetLastError();
 }

@@ -151,6 +151,19 @@ int32_t ab_sample(const ab_desc* desc, const float* scores, double density, uint
                   void* stream);
 
 /*
+ * Top-K truncation of the same score rows: the deterministic selection the SIP
+ * sentence of the AB-Attention abstract sets its sampler against (kept for
+ * estimator comparisons; the method itself samples with ab_sample).
+ *
+ * Per row (b, h, i): the same quantised scores w_j and budget K as ab_sample;
+ * the K sub-blocks with the largest w_j are kept, the lower index first among
+ * equal w_j, each with weight 1. Outputs as for ab_sample, with counts[row] = K.
+ * Rows of more than 16384 key sub-blocks are rejected with AB_ERR_SHAPE.
+ */
+int32_t ab_sample_topk(const ab_desc* desc, const float* scores, double density, int32_t* idx,
+                       float* weights, int32_t* counts, uint32_t* mask_bits, void* stream);
+
+/*
  * Weighted block-sparse attention forward (AB-Attention abstract, problem,
  * SIP and kernel sentences).
  *

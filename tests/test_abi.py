@@ -117,6 +117,26 @@ def test_density_errors(density):
     assert b"density" in lib.ab_last_error()
 
 
+@pytest.mark.parametrize("density", [0.0, float("nan"), 2.0])
+def test_topk_density_errors(density):
+    lib = _lib()
+    cd = _desc().c()
+    fake = ctypes.c_void_p(256)
+    assert lib.ab_sample_topk(ctypes.byref(cd), fake, ctypes.c_double(density), fake, fake, fake, None, None) == -4
+
+
+def test_topk_rejects_long_rows_and_nulls():
+    lib = _lib()
+    fake = ctypes.c_void_p(256)
+    # 16385 sub-blocks of 16 keys: one more than the top-K kernel takes
+    cd = _desc(N=16385 * 16, k_block=16).c()
+    assert lib.ab_sample_topk(ctypes.byref(cd), fake, ctypes.c_double(0.1), fake, fake, fake, None, None) == -2
+    assert b"16384" in lib.ab_last_error()
+    cd = _desc(N=16384 * 16, k_block=16).c()
+    assert lib.ab_sample_topk(ctypes.byref(cd), None, ctypes.c_double(0.1), fake, fake, fake, None, None) == -1
+    assert lib.ab_sample_topk(ctypes.byref(cd), fake, ctypes.c_double(0.1), fake, None, fake, None, None) == -1
+
+
 def test_python_binding_rejects_host_tensors():
     import torch
 

@@ -24,7 +24,7 @@ import torch
 
 import block_sparse_attention_ibcs_amd as ab
 import workloads
-from oracle import Params, dense_attention, kmeans_fp32, block_scores, sample_rows, sparse_ht_attention
+from oracle import Params, dense_attention, kmeans_fp32, block_scores, sample_rows, sparse_ht_attention, topk_rows
 from oracle.sip import SIP_ONE
 
 pytestmark = pytest.mark.gpu
@@ -424,6 +424,41 @@ def test_kmeans_rounding_case(dim):
     assert np.array_equal(assign.cpu().numpy()[0, 0], asg.astype(np.uint8))
     assert np.array_equal(sizes.cpu().numpy()[0, 0, 0], sz)
     assert np.array_equal(cent.cpu().numpy()[0, 0, 0].view(np.uint32), mu.view(np.uint32))
+
+
+@pytest.mark.parametrize("nkb,density", [(37, 0.3), (1024, 0.1), (1000, 1.0), (2363, 0.08), (4096, 0.5),
+                                         (4725, 0.05), (9000, 0.1), (16384, 0.02)])
+def test_topk_rows_any_length(nkb, density):
+    """Top-K truncation on synthetic score rows, bit-exact against the oracle: coarse
+    score values make ties at the cut common; zero, negative, NaN and >= 1 scores."""
+    _gpu()
+    Bk, Bq, H = 16, 128, 2
+    N = nkb * Bk - 5
+    desc = ab.Desc(1, H, N, 128, ab.AB_BF16, Bq, Bk, 8)
+    rng = np.random.default_rng(nkb + 1)
+    shape = (1, H, desc.nqb, nkb)
+    sc = (rng.integers(0, 9, size=shape) / 1024.0).astype(np.float32)
+    flat = sc.reshape(-1, nkb)
+    r = rng.integers(0, flat.shape[0], size=4)
+    flat[r[0], :3] = np.nan
+    flat[r[1], 1 % nkb] = -2.0
+    flat[r[2], 2 % nkb] = 1.5
+    flat[r[3], :] = 0.0
+    scores_d = torch.from_numpy(sc).cuda()
+    idx_d, wts_d, cnt_d, mask_d = ab.ab_sample_topk(desc, scores_d, density)
+    torch.cuda.synchronize()
+    idx, wts, cnt = idx_d.cpu().numpy(), wts_d.cpu().numpy(), cnt_d.cpu().numpy()
+    mask = mask_d.cpu().numpy().view(np.uint32)
+    K = max(1, min(nkb, math.floor(density * nkb + 0.5)))
+    assert np.all(cnt == K)
+    keys = [(0, int(x) // desc.nqb, int(x) % desc.nqb) for x in r] + [(0, 0, 0), (0, H - 1, desc.nqb - 1)]
+    for key, o in topk_rows(sc, density, keys).items():
+        b, h, i = key
+        assert np.array_equal(idx[b, h, i, :K], o["idx"]), key
+        assert np.all(wts[b, h, i, :K] == 1.0), key
+        assert np.array_equal(mask[b, h, i], o["mask"]), key
+    bits = np.unpackbits(mask.view(np.uint8), axis=-1, bitorder="little").sum(axis=-1)
+    assert np.array_equal(bits, cnt)
 
 
 def test_empty_rows_give_zero_output():
