@@ -47,6 +47,11 @@ def parse_args():
     ap.add_argument("--sweep", action="store_true",
                     help="gather-cost sweep on the 75600-token, 40-head shape: density {1, .25, .10, .05} x k_block "
                          "{16, 32, 64, 128}; one JSON line per point instead of the headline line")
+    ap.add_argument("--ablation", action="store_true",
+                    help="estimator comparison on --workload: relative L2 error of the layer output against dense "
+                         "attention for IBCS+SIP, IBCS+top-K, pooled (C=1)+SIP and pooled+top-K over density and "
+                         "k_block; one JSON line per point")
+    ap.add_argument("--ablation-seeds", type=int, default=4, help="SIP seeds per ablation point")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one device copy of this many MiB before timing (reference kernel for HBM counters)")
     return ap.parse_args()
@@ -180,6 +185,82 @@ def run_sweep(args):
         torch.cuda.empty_cache()
 
 
+ABLATION_DENSITIES = (0.05, 0.10, 0.25)
+ABLATION_K_BLOCKS = (16, 32, 64)
+
+
+def run_ablation(args):
+    """Estimator comparison. The dense reference is the attention kernel at density 1,
+    which keeps every sub-block with weight 1 (exact dense attention). For each k_block
+    and density: IBCS scores with the workload's C and pooled scores with C = 1, each
+    followed by SIP (args.ablation_seeds seeds, and the average of their outputs) and by
+    top-K truncation; the relative L2 error ||O - O_dense|| / ||O_dense|| over the whole
+    layer output is computed in fp32 on the device."""
+    import torch
+
+    import block_sparse_attention_ibcs_amd as ab
+    import workloads
+
+    w0 = workloads.get(args.workload)
+    q, k, v = workloads.generate(w0, seed=0)
+    dev = torch.device("cuda:0")
+    tdt = torch.bfloat16 if w0.dtype == "bf16" else torch.float32
+    qd, kd, vd = (torch.from_numpy(x).to(tdt).to(dev) for x in (q, k, v))
+    del q, k, v
+
+    def layer(desc, scores, rho, seed=None):
+        if seed is None:
+            idx, wts, cnt, _ = ab.ab_sample_topk(desc, scores, rho, want_mask=False)
+        else:
+            idx, wts, cnt, _ = ab.ab_sample(desc, scores, rho, seed, want_mask=False)
+        out, _ = ab.ab_attn_fwd(desc, qd, kd, vd, idx, wts, cnt, want_lse=False)
+        kept = float(cnt.to(torch.float64).sum().item()) / (cnt.numel() * desc.nkb)
+        return out.float(), kept
+
+    d_ref = ab.Desc.for_tensor(qd, w0.q_block, w0.k_block, w0.n_clusters, w0.kmeans_iters)
+    s_ref = ab.ab_score(d_ref, qd, kd)
+    o_dense, _ = layer(d_ref, s_ref, 1.0, seed=0)
+    ref_norm = float(torch.linalg.vector_norm(o_dense).item())
+    del s_ref
+
+    def rel(o):
+        return float(torch.linalg.vector_norm(o - o_dense).item()) / ref_norm
+
+    seeds = list(range(args.ablation_seeds))
+    for bk in ABLATION_K_BLOCKS:
+        scorers = {}
+        for name, c in (("ibcs", w0.n_clusters), ("pooled", 1)):
+            desc = ab.Desc.for_tensor(qd, w0.q_block, bk, c, w0.kmeans_iters)
+            scorers[name] = (desc, ab.ab_score(desc, qd, kd))
+        for rho in ABLATION_DENSITIES:
+            for name, (desc, scores) in scorers.items():
+                errs, kept, acc = [], [], None
+                for sd in seeds:
+                    o, kf = layer(desc, scores, rho, seed=sd)
+                    errs.append(rel(o))
+                    kept.append(kf)
+                    acc = o if acc is None else acc + o
+                mean_err = sum(errs) / len(errs)
+                sd_err = (sum((e - mean_err) ** 2 for e in errs) / max(1, len(errs) - 1)) ** 0.5
+                o_topk, kept_topk = layer(desc, scores, rho)
+                print(json.dumps({
+                    "ablation": "estimator",
+                    "workload": f"{args.workload}: B={w0.B} H={w0.H} N={w0.N} d={w0.d} Bq={w0.q_block} T={w0.kmeans_iters}",
+                    "k_block": bk,
+                    "density": rho,
+                    "scorer": f"{name} (C={desc.n_clusters})",
+                    "sip_rel_l2_mean": mean_err,
+                    "sip_rel_l2_sd": sd_err,
+                    "sip_kept": sum(kept) / len(kept),
+                    "sip_seed_average_rel_l2": rel(acc / len(seeds)),
+                    "topk_rel_l2": rel(o_topk),
+                    "topk_kept": kept_topk,
+                    "seeds": len(seeds),
+                }), flush=True)
+        del scorers
+        torch.cuda.empty_cache()
+
+
 def cpu_baseline(w, q, k, v, density, seed, budget_s):
     """Time the oracle (IBCS + SIP + weighted attention) on query blocks for about budget_s seconds:
     a seeded spread of the blocks of head 0, then of head 1, and so on."""
@@ -239,6 +320,9 @@ def main():
     ab.load_library()  # fails loudly if the HIP library is not built
     if args.sweep:
         run_sweep(args)
+        return
+    if args.ablation:
+        run_ablation(args)
         return
     w = workloads.get(args.workload)
     if args.k_block:
