@@ -193,8 +193,9 @@ def run_ablation(args):
     """Estimator comparison. The dense reference is the attention kernel at density 1,
     which keeps every sub-block with weight 1 (exact dense attention). For each k_block
     and density: IBCS scores with the workload's C and pooled scores with C = 1, each
-    followed by SIP (args.ablation_seeds seeds, and the average of their outputs) and by
-    top-K truncation; the relative L2 error ||O - O_dense|| / ||O_dense|| over the whole
+    followed by SIP with independent trials and with the systematic draw
+    (args.ablation_seeds seeds each, and the average of their outputs) and by top-K
+    truncation; the relative L2 error ||O - O_dense|| / ||O_dense|| over the whole
     layer output is computed in fp32 on the device."""
     import torch
 
@@ -208,9 +209,11 @@ def run_ablation(args):
     qd, kd, vd = (torch.from_numpy(x).to(tdt).to(dev) for x in (q, k, v))
     del q, k, v
 
-    def layer(desc, scores, rho, seed=None):
+    def layer(desc, scores, rho, seed=None, systematic=False):
         if seed is None:
             idx, wts, cnt, _ = ab.ab_sample_topk(desc, scores, rho, want_mask=False)
+        elif systematic:
+            idx, wts, cnt, _ = ab.ab_sample_systematic(desc, scores, rho, seed, want_mask=False)
         else:
             idx, wts, cnt, _ = ab.ab_sample(desc, scores, rho, seed, want_mask=False)
         out, _ = ab.ab_attn_fwd(desc, qd, kd, vd, idx, wts, cnt, want_lse=False)
@@ -242,6 +245,11 @@ def run_ablation(args):
                     acc = o if acc is None else acc + o
                 mean_err = sum(errs) / len(errs)
                 sd_err = (sum((e - mean_err) ** 2 for e in errs) / max(1, len(errs) - 1)) ** 0.5
+                sys_errs, sys_acc = [], None
+                for sd in seeds:
+                    o, _ = layer(desc, scores, rho, seed=sd, systematic=True)
+                    sys_errs.append(rel(o))
+                    sys_acc = o if sys_acc is None else sys_acc + o
                 o_topk, kept_topk = layer(desc, scores, rho)
                 print(json.dumps({
                     "ablation": "estimator",
@@ -253,6 +261,8 @@ def run_ablation(args):
                     "sip_rel_l2_sd": sd_err,
                     "sip_kept": sum(kept) / len(kept),
                     "sip_seed_average_rel_l2": rel(acc / len(seeds)),
+                    "systematic_rel_l2_mean": sum(sys_errs) / len(sys_errs),
+                    "systematic_seed_average_rel_l2": rel(sys_acc / len(seeds)),
                     "topk_rel_l2": rel(o_topk),
                     "topk_kept": kept_topk,
                     "seeds": len(seeds),

@@ -8,6 +8,7 @@ for) and passes pointers plus torch's current HIP stream.
 Stages (AB-Attention abstract, paperdot search page, query "Xing Ma"):
   ab_score     IBCS block-importance estimates per (query block, key sub-block)
   ab_sample    SIP draw with inverse-inclusion-probability weights
+  ab_sample_systematic  fixed-size systematic draw with the same inclusion probabilities
   ab_sample_topk  top-K truncation of the same scores (weight 1; for estimator comparisons)
   ab_attn_fwd  weighted block-sparse attention over the kept sub-blocks
 """
@@ -29,6 +30,7 @@ __all__ = [
     "ab_score",
     "ab_score_debug",
     "ab_sample",
+    "ab_sample_systematic",
     "ab_sample_topk",
     "ab_attn_fwd",
     "AbError",
@@ -47,6 +49,7 @@ EXPORTED_SYMBOLS = (
     "ab_score",
     "ab_score_debug",
     "ab_sample",
+    "ab_sample_systematic",
     "ab_sample_topk",
     "ab_attn_fwd",
 )
@@ -141,6 +144,8 @@ def load_library():
     lib.ab_score_debug.argtypes = [D, P, P, P, P, P]
     lib.ab_sample.restype = ctypes.c_int32
     lib.ab_sample.argtypes = [D, P, ctypes.c_double, ctypes.c_uint64, P, P, P, P, P]
+    lib.ab_sample_systematic.restype = ctypes.c_int32
+    lib.ab_sample_systematic.argtypes = [D, P, ctypes.c_double, ctypes.c_uint64, P, P, P, P, P]
     lib.ab_sample_topk.restype = ctypes.c_int32
     lib.ab_sample_topk.argtypes = [D, P, ctypes.c_double, P, P, P, P, P]
     lib.ab_attn_fwd.restype = ctypes.c_int32
@@ -246,6 +251,28 @@ def ab_sample(desc: Desc, scores, density: float, seed: int, idx=None, weights=N
     rc = lib.ab_sample(ctypes.byref(cd), _ptr(scores), float(density), int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(idx),
                        _ptr(weights), _ptr(counts), _ptr(mask), _stream(stream))
     _check(rc, "ab_sample")
+    return idx, weights, counts, mask
+
+
+def ab_sample_systematic(desc: Desc, scores, density: float, seed: int, idx=None, weights=None, counts=None,
+                         mask=None, want_mask=True, stream=None):
+    """Systematic draw: (idx int32, weights fp32 [B,H,NQB,NKB], counts int32 [B,H,NQB], mask uint32 or None)."""
+    lib = load_library()
+    rows = (desc.B, desc.H, desc.nqb)
+    _need(scores, "scores", rows + (desc.nkb,), torch.float32)
+    dev = scores.device
+    if idx is None:
+        idx = torch.empty(rows + (desc.nkb,), dtype=torch.int32, device=dev)
+    if weights is None:
+        weights = torch.empty(rows + (desc.nkb,), dtype=torch.float32, device=dev)
+    if counts is None:
+        counts = torch.empty(rows, dtype=torch.int32, device=dev)
+    if mask is None and want_mask:
+        mask = torch.empty(rows + (-(-desc.nkb // 32),), dtype=torch.int32, device=dev)
+    cd = desc.c()
+    rc = lib.ab_sample_systematic(ctypes.byref(cd), _ptr(scores), float(density), int(seed) & 0xFFFFFFFFFFFFFFFF,
+                                  _ptr(idx), _ptr(weights), _ptr(counts), _ptr(mask), _stream(stream))
+    _check(rc, "ab_sample_systematic")
     return idx, weights, counts, mask
 
 

@@ -66,9 +66,11 @@ hipError_t launch_score_lse(const Dims& D, const ScoreWs& L, const void* k, cons
                             float* ell, float* lpart, hipStream_t s);
 hipError_t launch_score_assemble(const Dims& D, const ScoreWs& L, const float* ell, const float* lpart,
                                  const int32_t* sizes, float* scores, hipStream_t s);
+// systematic: fixed-size systematic draw instead of independent trials (rows of at
+// most kTopkMaxNkb sub-blocks)
 hipError_t launch_sample(const Dims& D, const float* scores, int K, uint64_t seed, int32_t* idx,
-                         float* weights, int32_t* counts, uint32_t* mask, hipStream_t s);
-constexpr int kTopkMaxNkb = 16384;  // longest row the top-K kernel takes
+                         float* weights, int32_t* counts, uint32_t* mask, hipStream_t s, bool systematic);
+constexpr int kTopkMaxNkb = 16384;  // longest row the top-K and systematic kernels take
 hipError_t launch_topk(const Dims& D, const float* scores, int K, int32_t* idx, float* weights, int32_t* counts,
                        uint32_t* mask, hipStream_t s);
 hipError_t launch_attn_fwd(const Dims& D, const void* q, const void* k, const void* v, const int32_t* idx,

@@ -183,8 +183,26 @@ int32_t ab_sample(const ab_desc* desc, const float* scores, double density, uint
   const int K = budget_blocks(density, P.nkb);
   if ((rc = check_device())) return rc;
   hipError_t e = ab::launch_sample(P, scores, K, seed, idx, weights, counts, mask_bits,
-                                   static_cast<hipStream_t>(stream));
+                                   static_cast<hipStream_t>(stream), false);
   if (e != hipSuccess) return hip_fail(e, "sampler launch");
+  return AB_OK;
+}
+
+int32_t ab_sample_systematic(const ab_desc* desc, const float* scores, double density, uint64_t seed, int32_t* idx,
+                             float* weights, int32_t* counts, uint32_t* mask_bits, void* stream) {
+  g_err[0] = 0;
+  ab::Dims P;
+  int32_t rc = make_dims(desc, &P);
+  if (rc) return rc;
+  if (!scores || !idx || !weights || !counts) return fail(AB_ERR_NULL, "scores, idx, weights and counts must be non-NULL");
+  if (!(density > 0.0 && density <= 1.0)) return fail(AB_ERR_DENSITY, "density %g not in (0, 1]", density);
+  if (P.nkb > ab::kTopkMaxNkb)
+    return fail(AB_ERR_SHAPE, "systematic sampling takes rows of at most %d sub-blocks (got %d)", ab::kTopkMaxNkb, P.nkb);
+  const int K = budget_blocks(density, P.nkb);
+  if ((rc = check_device())) return rc;
+  hipError_t e = ab::launch_sample(P, scores, K, seed, idx, weights, counts, mask_bits,
+                                   static_cast<hipStream_t>(stream), true);
+  if (e != hipSuccess) return hip_fail(e, "systematic sampler launch");
   return AB_OK;
 }
 

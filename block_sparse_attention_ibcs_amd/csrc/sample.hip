@@ -231,7 +231,41 @@ __device__ __forceinline__ int wave_sum_i32(int v) {
 constexpr int kLaneElems = 16;          // sub-blocks per lane per chunk
 constexpr int kChunk = 64 * kLaneElems; // sub-blocks per chunk
 
-template <int NCH>
+
+// Inclusive prefix sum over the wave in lane order.
+__device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t v) {
+  const int lane = threadIdx.x & 63;
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint64_t y = __shfl_up(v, off, 64);
+    if (lane >= off) v += y;
+  }
+  return v;
+}
+
+// Systematic draw of one lane's 16 blocks: the row's points U + m * 2^24 (m >= 0)
+// against the half-open intervals [C_j, C_j + t_j) of the cumulative thresholds;
+// c0 is C of the lane's first block.
+__device__ __forceinline__ int64_t points_below(uint64_t x, uint32_t U) {
+  return x > U ? int64_t((x - 1 - U) >> 24) + 1 : 0;
+}
+__device__ __forceinline__ uint32_t systematic_keep16(const uint32_t (&t)[kLaneElems], uint32_t valid, uint64_t c0,
+                                                      uint32_t U) {
+  uint32_t keep = 0u;
+  uint64_t c = c0;
+  int64_t below = points_below(c, U);
+#pragma unroll
+  for (int e = 0; e < kLaneElems; ++e) {
+    if ((valid >> e) & 1u) {
+      c += t[e];
+      const int64_t nb = points_below(c, U);
+      if (nb > below) keep |= 1u << e;
+      below = nb;
+    }
+  }
+  return keep;
+}
+
+template <int NCH, bool SYS>
 __global__ __launch_bounds__(256) void sample_wave_kernel(Dims P, int K, int rows, uint32_t seed_lo,
                                                           uint32_t seed_hi, const float* __restrict__ scores,
                                                           int32_t* __restrict__ idx, float* __restrict__ weights,
@@ -312,23 +346,44 @@ __global__ __launch_bounds__(256) void sample_wave_kernel(Dims P, int K, int row
   uint32_t keep[NCH];
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
-    keep[c] = 0u;
-    const int g0 = (c * kChunk + lane * kLaneElems) >> 2;
 #pragma unroll
-    for (int g = 0; g < kLaneElems / 4; ++g) {
-      if (!((valid[c] >> (4 * g)) & 0xFu)) continue;
-      const uint4 r = philox4x32_10(uint32_t(g0 + g), uint32_t(i), uint32_t(h), uint32_t(b), seed_lo, seed_hi);
-      const uint32_t rr[4] = {r.x, r.y, r.z, r.w};
+    for (int e = 0; e < kLaneElems; ++e) {
+      uint32_t t = kOne;
+      if (!((cap[c] >> e) & 1u)) {
+        const uint32_t q = floor_div_est(room * uint64_t(w[c][e]) * uint64_t(kOne), S, rS);
+        t = q > 0u ? q : 1u;
+      }
+      w[c][e] = ((valid[c] >> e) & 1u) ? t : 0u;
+    }
+  }
+  if constexpr (SYS) {
+    // one uniform per row; cumulative thresholds in index order (chunk, lane, element)
+    const uint32_t U = philox4x32_10(0xFFFFFFFFu, uint32_t(i), uint32_t(h), uint32_t(b), seed_lo, seed_hi).x >> 8;
+    uint64_t cbase = 0;
 #pragma unroll
-      for (int e4 = 0; e4 < 4; ++e4) {
-        const int e = 4 * g + e4;
-        uint32_t t = kOne;
-        if (!((cap[c] >> e) & 1u)) {
-          const uint32_t q = floor_div_est(room * uint64_t(w[c][e]) * uint64_t(kOne), S, rS);
-          t = q > 0u ? q : 1u;
+    for (int c = 0; c < NCH; ++c) {
+      uint32_t lsum = 0;
+#pragma unroll
+      for (int e = 0; e < kLaneElems; ++e) lsum += w[c][e];
+      const uint64_t incl = wave_incl_scan_u64(lsum);
+      keep[c] = systematic_keep16(w[c], valid[c], cbase + incl - lsum, U);
+      cbase += __shfl(incl, 63, 64);
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      keep[c] = 0u;
+      const int g0 = (c * kChunk + lane * kLaneElems) >> 2;
+#pragma unroll
+      for (int g = 0; g < kLaneElems / 4; ++g) {
+        if (!((valid[c] >> (4 * g)) & 0xFu)) continue;
+        const uint4 r = philox4x32_10(uint32_t(g0 + g), uint32_t(i), uint32_t(h), uint32_t(b), seed_lo, seed_hi);
+        const uint32_t rr[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const int e = 4 * g + e4;
+          if (((valid[c] >> e) & 1u) && (rr[e4] >> 8) < w[c][e]) keep[c] |= 1u << e;
         }
-        w[c][e] = t;
-        if (((valid[c] >> e) & 1u) && (rr[e4] >> 8) < t) keep[c] |= 1u << e;
       }
     }
   }
@@ -371,7 +426,7 @@ __global__ __launch_bounds__(256) void sample_wave_kernel(Dims P, int K, int row
 // compaction is a workgroup prefix sum per chunk.
 constexpr int kBlockChunk = kThreads * kLaneElems;
 
-template <int NCH>
+template <int NCH, bool SYS>
 __global__ __launch_bounds__(kThreads) void sample_block_kernel(Dims P, int K, uint32_t seed_lo, uint32_t seed_hi,
                                                                 const float* __restrict__ scores,
                                                                 int32_t* __restrict__ idx,
@@ -454,23 +509,53 @@ __global__ __launch_bounds__(kThreads) void sample_block_kernel(Dims P, int K, u
   uint32_t keep[NCH];
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
-    keep[c] = 0u;
-    const int g0 = (c * kBlockChunk + tid * kLaneElems) >> 2;
 #pragma unroll
-    for (int g = 0; g < kLaneElems / 4; ++g) {
-      if (!((valid[c] >> (4 * g)) & 0xFu)) continue;
-      const uint4 r = philox4x32_10(uint32_t(g0 + g), uint32_t(i), uint32_t(h), uint32_t(b), seed_lo, seed_hi);
-      const uint32_t rr[4] = {r.x, r.y, r.z, r.w};
+    for (int e = 0; e < kLaneElems; ++e) {
+      uint32_t t = kOne;
+      if (!((cap[c] >> e) & 1u)) {
+        const uint32_t q = floor_div_est(room * uint64_t(w[c][e]) * uint64_t(kOne), S, rS);
+        t = q > 0u ? q : 1u;
+      }
+      w[c][e] = ((valid[c] >> e) & 1u) ? t : 0u;
+    }
+  }
+  if constexpr (SYS) {
+    __shared__ uint64_t wtot64[4];
+    const uint32_t U = philox4x32_10(0xFFFFFFFFu, uint32_t(i), uint32_t(h), uint32_t(b), seed_lo, seed_hi).x >> 8;
+    uint64_t cbase = 0;
 #pragma unroll
-      for (int e4 = 0; e4 < 4; ++e4) {
-        const int e = 4 * g + e4;
-        uint32_t t = kOne;
-        if (!((cap[c] >> e) & 1u)) {
-          const uint32_t q = floor_div_est(room * uint64_t(w[c][e]) * uint64_t(kOne), S, rS);
-          t = q > 0u ? q : 1u;
+    for (int c = 0; c < NCH; ++c) {
+      uint32_t lsum = 0;
+#pragma unroll
+      for (int e = 0; e < kLaneElems; ++e) lsum += w[c][e];
+      const uint64_t incl = wave_incl_scan_u64(lsum);
+      __syncthreads();  // wtot64 of the previous chunk is consumed
+      if (lane == 63) wtot64[wave] = incl;
+      __syncthreads();
+      uint64_t woff = 0, tot = 0;
+#pragma unroll
+      for (int wv = 0; wv < kThreads / 64; ++wv) {
+        woff += wv < wave ? wtot64[wv] : 0;
+        tot += wtot64[wv];
+      }
+      keep[c] = systematic_keep16(w[c], valid[c], cbase + woff + incl - lsum, U);
+      cbase += tot;
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      keep[c] = 0u;
+      const int g0 = (c * kBlockChunk + tid * kLaneElems) >> 2;
+#pragma unroll
+      for (int g = 0; g < kLaneElems / 4; ++g) {
+        if (!((valid[c] >> (4 * g)) & 0xFu)) continue;
+        const uint4 r = philox4x32_10(uint32_t(g0 + g), uint32_t(i), uint32_t(h), uint32_t(b), seed_lo, seed_hi);
+        const uint32_t rr[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const int e = 4 * g + e4;
+          if (((valid[c] >> e) & 1u) && (rr[e4] >> 8) < w[c][e]) keep[c] |= 1u << e;
         }
-        w[c][e] = t;
-        if (((valid[c] >> e) & 1u) && (rr[e4] >> 8) < t) keep[c] |= 1u << e;
       }
     }
   }
@@ -654,25 +739,25 @@ __global__ __launch_bounds__(kThreads) void topk_block_kernel(Dims P, int K, con
 
 }  // namespace
 
-hipError_t launch_sample(const Dims& P, const float* scores, int K, uint64_t seed, int32_t* idx, float* weights,
-                         int32_t* counts, uint32_t* mask, hipStream_t s) {
+template <bool SYS>
+hipError_t launch_sample_mode(const Dims& P, const float* scores, int K, uint64_t seed, int32_t* idx, float* weights,
+                              int32_t* counts, uint32_t* mask, hipStream_t s) {
   const int rows = P.B * P.H * P.nqb;
   const uint32_t lo = uint32_t(seed), hi = uint32_t(seed >> 32);
-  const int nch = ceil_div(P.nkb, kChunk);
   const dim3 grid(ceil_div(rows, 4)), block(256);
-  switch (nch) {
-    case 1: hipLaunchKernelGGL(sample_wave_kernel<1>, grid, block, 0, s, P, K, rows, lo, hi, scores, idx, weights, counts, mask); break;
-    case 2: hipLaunchKernelGGL(sample_wave_kernel<2>, grid, block, 0, s, P, K, rows, lo, hi, scores, idx, weights, counts, mask); break;
-    case 3: hipLaunchKernelGGL(sample_wave_kernel<3>, grid, block, 0, s, P, K, rows, lo, hi, scores, idx, weights, counts, mask); break;
-    case 4: hipLaunchKernelGGL(sample_wave_kernel<4>, grid, block, 0, s, P, K, rows, lo, hi, scores, idx, weights, counts, mask); break;
+  switch (ceil_div(P.nkb, kChunk)) {
+    case 1: hipLaunchKernelGGL((sample_wave_kernel<1, SYS>), grid, block, 0, s, P, K, rows, lo, hi, scores, idx, weights, counts, mask); break;
+    case 2: hipLaunchKernelGGL((sample_wave_kernel<2, SYS>), grid, block, 0, s, P, K, rows, lo, hi, scores, idx, weights, counts, mask); break;
+    case 3: hipLaunchKernelGGL((sample_wave_kernel<3, SYS>), grid, block, 0, s, P, K, rows, lo, hi, scores, idx, weights, counts, mask); break;
+    case 4: hipLaunchKernelGGL((sample_wave_kernel<4, SYS>), grid, block, 0, s, P, K, rows, lo, hi, scores, idx, weights, counts, mask); break;
     default: {
-      const int nchb = ceil_div(P.nkb, kBlockChunk);
       const dim3 g(rows), t(kThreads);
-      switch (nchb) {
-        case 2: hipLaunchKernelGGL(sample_block_kernel<2>, g, t, 0, s, P, K, lo, hi, scores, idx, weights, counts, mask); break;
-        case 3: hipLaunchKernelGGL(sample_block_kernel<3>, g, t, 0, s, P, K, lo, hi, scores, idx, weights, counts, mask); break;
-        case 4: hipLaunchKernelGGL(sample_block_kernel<4>, g, t, 0, s, P, K, lo, hi, scores, idx, weights, counts, mask); break;
+      switch (ceil_div(P.nkb, kBlockChunk)) {
+        case 2: hipLaunchKernelGGL((sample_block_kernel<2, SYS>), g, t, 0, s, P, K, lo, hi, scores, idx, weights, counts, mask); break;
+        case 3: hipLaunchKernelGGL((sample_block_kernel<3, SYS>), g, t, 0, s, P, K, lo, hi, scores, idx, weights, counts, mask); break;
+        case 4: hipLaunchKernelGGL((sample_block_kernel<4, SYS>), g, t, 0, s, P, K, lo, hi, scores, idx, weights, counts, mask); break;
         default: {
+          if (SYS) return hipErrorInvalidValue;  // rejected on the host before this point
           const size_t lds = size_t(ceil_div(P.nkb, 32)) * 4;
           hipLaunchKernelGGL(sample_kernel, g, t, lds, s, P, K, lo, hi, scores, idx, weights, counts, mask);
         }
@@ -680,6 +765,12 @@ hipError_t launch_sample(const Dims& P, const float* scores, int K, uint64_t see
     }
   }
   return hipGetLastError();
+}
+
+hipError_t launch_sample(const Dims& P, const float* scores, int K, uint64_t seed, int32_t* idx, float* weights,
+                         int32_t* counts, uint32_t* mask, hipStream_t s, bool systematic) {
+  return systematic ? launch_sample_mode<true>(P, scores, K, seed, idx, weights, counts, mask, s)
+                    : launch_sample_mode<false>(P, scores, K, seed, idx, weights, counts, mask, s);
 }
 
 hipError_t launch_topk(const Dims& P, const float* scores, int K, int32_t* idx, float* weights, int32_t* counts,

@@ -151,6 +151,24 @@ int32_t ab_sample(const ab_desc* desc, const float* scores, double density, uint
                   void* stream);
 
 /*
+ * Fixed-size (systematic) sampling with the same inclusion probabilities as
+ * ab_sample: the other standard design for sampling with known inclusion
+ * probabilities (AB-Attention abstract, SIP sentence, which fixes no design).
+ *
+ * Per row (b, h, i): thresholds t_j exactly as ab_sample; one 24-bit uniform
+ * U = word 0 of Philox4x32-10(key = (seed mod 2^32, seed >> 32), counter =
+ * (2^32 - 1, i, h, b)) >> 8; with C_j = t_0 + ... + t_{j-1}, block j is kept
+ * iff [C_j, C_j + t_j) holds a point U + m*2^24 (m >= 0), so it is kept with
+ * probability t_j/2^24 exactly and a row keeps floor(T/2^24) or one more block
+ * (T = sum of t_j, about K*2^24); weight fp32(2^24)/fp32(t_j). Outputs as for
+ * ab_sample. Rows of more than 16384 key sub-blocks are rejected with
+ * AB_ERR_SHAPE.
+ */
+int32_t ab_sample_systematic(const ab_desc* desc, const float* scores, double density, uint64_t seed,
+                             int32_t* idx, float* weights, int32_t* counts, uint32_t* mask_bits,
+                             void* stream);
+
+/*
  * Top-K truncation of the same score rows: the deterministic selection the SIP
  * sentence of the AB-Attention abstract sets its sampler against (kept for
  * estimator comparisons; the method itself samples with ab_sample).

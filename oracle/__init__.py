@@ -25,6 +25,7 @@ from .philox import philox4x32_10
 from .ibcs import kmeans_fp32, block_scores, round_bf16
 from .sip import quantize_scores, budget, inclusion_thresholds, sample_rows, SIP_ONE
 from .topk import topk_rows
+from .systematic import sample_rows_systematic
 from .attention import dense_attention, sparse_ht_attention
 from .pipeline import Params, run_blocks
 
@@ -38,6 +39,7 @@ __all__ = [
     "inclusion_thresholds",
     "sample_rows",
     "topk_rows",
+    "sample_rows_systematic",
     "SIP_ONE",
     "dense_attention",
     "sparse_ht_attention",

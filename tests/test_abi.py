@@ -125,6 +125,16 @@ def test_topk_density_errors(density):
     assert lib.ab_sample_topk(ctypes.byref(cd), fake, ctypes.c_double(density), fake, fake, fake, None, None) == -4
 
 
+def test_systematic_validation():
+    lib = _lib()
+    fake = ctypes.c_void_p(256)
+    cd = _desc().c()
+    assert lib.ab_sample_systematic(ctypes.byref(cd), fake, ctypes.c_double(0.0), 0, fake, fake, fake, None, None) == -4
+    assert lib.ab_sample_systematic(ctypes.byref(cd), fake, ctypes.c_double(0.1), 0, None, fake, fake, None, None) == -1
+    cd = _desc(N=16385 * 16, k_block=16).c()
+    assert lib.ab_sample_systematic(ctypes.byref(cd), fake, ctypes.c_double(0.1), 0, fake, fake, fake, None, None) == -2
+
+
 def test_topk_rejects_long_rows_and_nulls():
     lib = _lib()
     fake = ctypes.c_void_p(256)

@@ -24,7 +24,8 @@ import torch
 
 import block_sparse_attention_ibcs_amd as ab
 import workloads
-from oracle import Params, dense_attention, kmeans_fp32, block_scores, sample_rows, sparse_ht_attention, topk_rows
+from oracle import (Params, dense_attention, kmeans_fp32, block_scores, sample_rows, sample_rows_systematic,
+                    sparse_ht_attention, topk_rows)
 from oracle.sip import SIP_ONE
 
 pytestmark = pytest.mark.gpu
@@ -457,6 +458,47 @@ def test_topk_rows_any_length(nkb, density):
         assert np.array_equal(idx[b, h, i, :K], o["idx"]), key
         assert np.all(wts[b, h, i, :K] == 1.0), key
         assert np.array_equal(mask[b, h, i], o["mask"]), key
+    bits = np.unpackbits(mask.view(np.uint8), axis=-1, bitorder="little").sum(axis=-1)
+    assert np.array_equal(bits, cnt)
+
+
+@pytest.mark.parametrize("nkb,density", [(37, 0.3), (1024, 0.1), (1000, 1.0), (2363, 0.08), (4096, 0.5),
+                                         (4725, 0.05), (7425, 0.08), (16384, 0.02)])
+def test_systematic_rows_any_length(nkb, density):
+    """Systematic draw on synthetic score rows, bit-exact against the oracle (indices,
+    weights, counts, mask bits) on every row-length class it takes; every row keeps
+    floor(T / 2^24) or one more block."""
+    _gpu()
+    Bk, Bq, H = 16, 128, 2
+    N = nkb * Bk - 9
+    desc = ab.Desc(1, H, N, 128, ab.AB_BF16, Bq, Bk, 8)
+    rng = np.random.default_rng(nkb + 7)
+    shape = (1, H, desc.nqb, nkb)
+    logits = rng.standard_normal(shape) * 2.0
+    logits[rng.random(shape) < 6.0 / nkb] += 10.0
+    sc = np.exp(logits - logits.max(axis=-1, keepdims=True))
+    sc = (sc / sc.sum(axis=-1, keepdims=True)).astype(np.float32)
+    flat = sc.reshape(-1, nkb)
+    r = rng.integers(0, flat.shape[0], size=3)
+    flat[r[0], :2] = np.nan
+    flat[r[1], :] = 0.0
+    flat[r[2], 0] = 4.0
+    scores_d = torch.from_numpy(sc).cuda()
+    seed = 0xFEEDFACE12345 + nkb
+    idx_d, wts_d, cnt_d, mask_d = ab.ab_sample_systematic(desc, scores_d, density, seed)
+    torch.cuda.synchronize()
+    idx, wts, cnt = idx_d.cpu().numpy(), wts_d.cpu().numpy(), cnt_d.cpu().numpy()
+    mask = mask_d.cpu().numpy().view(np.uint32)
+    keys = [(0, int(x) // desc.nqb, int(x) % desc.nqb) for x in r] + [(0, 0, 0), (0, H - 1, desc.nqb - 1)]
+    for key, o in sample_rows_systematic(sc, density, seed, keys).items():
+        b, h, i = key
+        c = int(cnt[b, h, i])
+        assert c == o["count"], key
+        assert np.array_equal(idx[b, h, i, :c], o["idx"]), key
+        assert np.array_equal(wts[b, h, i, :c].view(np.uint32), o["weight"].view(np.uint32)), key
+        assert np.array_equal(mask[b, h, i], o["mask"]), key
+        T = int(o["thresh"].astype(np.int64).sum())
+        assert c in (T >> 24, (T >> 24) + 1), key
     bits = np.unpackbits(mask.view(np.uint8), axis=-1, bitorder="little").sum(axis=-1)
     assert np.array_equal(bits, cnt)
 
