@@ -44,6 +44,9 @@ def parse_args():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="wall time budget of the CPU oracle sample")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay one step captured in a HIP graph instead of launching the three calls eagerly "
+                         "(measured: no faster, the launches already run ahead of the GPU)")
     ap.add_argument("--sweep", action="store_true",
                     help="gather-cost sweep on the 75600-token, 40-head shape: density {1, .25, .10, .05} x k_block "
                          "{16, 32, 64, 128}; one JSON line per point instead of the headline line")
@@ -382,12 +385,28 @@ def main():
             ev["sample"].append((e[1], e[2]))
             ev["attn"].append((e[2], e[3]))
 
+    # One step captured in a HIP graph (the same kernels on the same buffers, launched as
+    # one graph): the timed loop replays it. The path issues no memsets, so the graph
+    # holds kernel nodes only.
+    run = step
+    if args.graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for _ in range(3):
+                step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        run = graph.replay
     for _ in range(args.warmup):
-        step()
+        run()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step()
+        run()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall / args.steps * 1e3
@@ -425,6 +444,7 @@ def main():
             "density": density,
             "realised_density": realised,
             "stage_ms": stage_ms,
+            "hip_graph": bool(args.graph),
             "attn_actual_tflops": achieved,
             "attn_dense_equivalent_tflops": dense / attn_s / 1e12,
             "layer_actual_tflops_excl_scorer": actual_flops / (ms_per_step / 1e3) / 1e12,
