@@ -49,13 +49,21 @@ struct LseState {
 template <int BK>
 __device__ __forceinline__ void lse_block(const f32x16_t& acc, LseState& st, float c2, int kb, int key_end,
                                           int half, bool row_ok, float* ell_row, int C, int nkb) {
+  // This lane's 16 keys: e < 8 lie in the block's first 16 keys, e >= 8 in the last 16.
   float ev[16];
+  float s0, s1;  // this lane's sums over its keys of the first and of the last 16
+  auto exps = [&]() {
 #pragma unroll
-  for (int e = 0; e < 16; ++e) ev[e] = fast_exp2(__builtin_fmaf(acc[e], c2, -st.mref));
-  float s_own = ev[0];
+    for (int e = 0; e < 16; ++e) ev[e] = fast_exp2(__builtin_fmaf(acc[e], c2, -st.mref));
+    s0 = ev[0];
 #pragma unroll
-  for (int e = 1; e < 16; ++e) s_own += ev[e];
-  float s_pair = pair_sum(s_own);
+    for (int e = 1; e < 8; ++e) s0 += ev[e];
+    s1 = ev[8];
+#pragma unroll
+    for (int e = 9; e < 16; ++e) s1 += ev[e];
+  };
+  exps();
+  float s_pair = pair_sum(s0 + s1);
   // rebase when the reference is unset (first block) or a sum would pass 2^64
   if (__builtin_amdgcn_ballot_w64(!(s_pair < 1.8446744e19f)) != 0) {
     float bm = acc[0];
@@ -66,24 +74,19 @@ __device__ __forceinline__ void lse_block(const f32x16_t& acc, LseState& st, flo
     st.tot *= f;
     st.sub *= f;
     st.mref = nref;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) ev[e] = fast_exp2(__builtin_fmaf(acc[e], c2, -st.mref));
-    s_own = ev[0];
-#pragma unroll
-    for (int e = 1; e < 16; ++e) s_own += ev[e];
-    s_pair = pair_sum(s_own);
+    exps();
+    s_pair = pair_sum(s0 + s1);
   }
   st.tot += s_pair;
   if constexpr (BK == 16) {
-    float s0 = 0.0f, s1 = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) s0 += ev[e];
-#pragma unroll
-    for (int e = 8; e < 16; ++e) s1 += ev[e];
-    s0 = pair_sum(s0);
-    s1 = pair_sum(s1);
+    // half 0 stores the first sub-block and needs the other half's s0; half 1 the
+    // second and needs s1: one exchange carries both
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(half ? s0 : s1), __float_as_uint(half ? s0 : s1),
+                                                    false, false);
+    const float other = __uint_as_float(half ? r[0] : r[1]);
+    const float sub = (half ? s1 : s0) + other;
     const int j = kb / 16 + half;
-    if (row_ok && j < nkb) ell_row[size_t(j) * C] = st.mref + fast_log2(half ? s1 : s0);
+    if (row_ok && j < nkb) ell_row[size_t(j) * C] = st.mref + fast_log2(sub);
   } else if constexpr (BK == 32) {
     if (row_ok && half == 0) ell_row[size_t(kb / 32) * C] = st.mref + fast_log2(s_pair);
   } else {
