@@ -322,15 +322,26 @@ ScoreWs score_ws_layout(const Dims& D, int num_cus) {
   ScoreWs L{};
   auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
   const size_t heads = size_t(D.B) * D.H;
-  // key splits: enough (row tile, split, head) workgroups for two waves of the chip
+  // Key splits: all (row tile, split, head) workgroups do the same work, and a CU holds
+  // three of them at once (occupancy 3), so the time goes as (rounds of resident
+  // workgroups) x (keys per workgroup), plus about one tile of set-up per workgroup;
+  // take the split count that minimises it (at least two 64-key tiles per split).
   int splits = 1;
   if (D.bf16) {
     const long tiles = long(ceil_div(D.mrows, 256)) * long(heads);
-    const long want = 2L * num_cus;
-    while (tiles * splits < want && splits < 64) splits *= 2;
-    // at least two 64-key tiles per split
-    const int max_splits = max(1, ceil_div(D.N, 256));
-    splits = min(splits, max_splits);
+    const long slots = 3L * max(1, num_cus);
+    const int max_splits = min(64, max(1, ceil_div(D.N, 256)));
+    long best = -1;
+    for (int s = 1; s <= max_splits; ++s) {
+      const long sk = long(ceil_div(ceil_div(D.N, s), 128)) * 128;
+      const long s_eff = (D.N + sk - 1) / sk;
+      const long rounds = (tiles * s_eff + slots - 1) / slots;
+      const long cost = rounds * (sk + 64);
+      if (best < 0 || cost < best) {
+        best = cost;
+        splits = s;
+      }
+    }
   }
   int split_keys = ceil_div(ceil_div(D.N, splits), 128) * 128;
   splits = ceil_div(D.N, split_keys);
