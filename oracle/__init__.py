@@ -13,6 +13,11 @@ reweighted by the inverse inclusion probability so one pass estimates dense
 attention (SIP sentence). The pages give no formulas; every constant and rule
 the abstract leaves open is a stated reading, listed in the module that uses it.
 
+The FP8 variant (``fp8``) follows the VC-Attention page (iitak.ru news on
+MiniMax-H3): 8-bit products, V-Smooth (per-block mean subtracted, residual
+quantised) and ExpCast-FP8 (the FP8 byte of a probability from one linear
+formula with rounding); quantisation codes are exact, the attention is float64.
+
 Precision: k-means is an exact-operation fp32 specification (both sides must
 produce identical bits), the sampler is integer arithmetic on fp32 scores, and
 everything else is float64.
@@ -28,6 +33,7 @@ from .topk import topk_rows
 from .systematic import sample_rows_systematic
 from .attention import dense_attention, sparse_ht_attention
 from .pipeline import Params, run_blocks
+from . import fp8
 
 __all__ = [
     "philox4x32_10",
