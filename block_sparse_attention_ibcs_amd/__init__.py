@@ -37,6 +37,8 @@ __all__ = [
     "AB_BF16",
     "AB_F32",
     "EXPORTED_SYMBOLS",
+    "Fp8Operands",
+    "ab_fp8_prepare",
 ]
 
 AB_BF16 = 0
@@ -52,6 +54,8 @@ EXPORTED_SYMBOLS = (
     "ab_sample_systematic",
     "ab_sample_topk",
     "ab_attn_fwd",
+    "ab_fp8_workspace_size",
+    "ab_fp8_prepare",
 )
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -150,6 +154,10 @@ def load_library():
     lib.ab_sample_topk.argtypes = [D, P, ctypes.c_double, P, P, P, P, P]
     lib.ab_attn_fwd.restype = ctypes.c_int32
     lib.ab_attn_fwd.argtypes = [D, P, P, P, P, P, P, P, P, P]
+    lib.ab_fp8_workspace_size.restype = ctypes.c_size_t
+    lib.ab_fp8_workspace_size.argtypes = [D]
+    lib.ab_fp8_prepare.restype = ctypes.c_int32
+    lib.ab_fp8_prepare.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     _lib = lib
     return lib
 
@@ -317,3 +325,41 @@ def ab_attn_fwd(desc: Desc, q, k, v, idx, weights, counts, out=None, lse=None, w
                          _ptr(out), _ptr(lse), _stream(stream))
     _check(rc, "ab_attn_fwd")
     return out, lse
+
+
+class Fp8Operands:
+    """Device tensors of ab_fp8_prepare's outputs (layouts as in include/ab_attn.h)."""
+
+    def __init__(self, desc: Desc, device):
+        B, H, N, d = desc.B, desc.H, desc.N, desc.d
+        u8 = torch.uint8
+        self.qcode = torch.empty((B, H, N, d), dtype=u8, device=device)
+        self.qscale = torch.empty((B, H, desc.nqb), dtype=torch.float32, device=device)
+        self.kcode = torch.empty((B, H, N, d), dtype=u8, device=device)
+        self.kscale = torch.empty((B, H, desc.nkb), dtype=torch.float32, device=device)
+        self.vcode = torch.empty((B, H, desc.nkb, 2, d, desc.k_block // 2), dtype=u8, device=device)
+        self.vmean = torch.empty((B, H, desc.nkb, d), dtype=torch.bfloat16, device=device)
+        self.vscale = torch.empty((B, H), dtype=torch.float32, device=device)
+        self.vmean_scaled = torch.empty((B, H, desc.nkb, d), dtype=torch.int32, device=device)
+        lib = load_library()
+        cd = desc.c()
+        nbytes = int(lib.ab_fp8_workspace_size(ctypes.byref(cd)))
+        if nbytes == 0:
+            raise AbError(-2, "ab_fp8_workspace_size", lib.ab_last_error().decode())
+        self.ws = torch.empty((nbytes + 3) // 4, dtype=torch.int32, device=device)
+
+
+def ab_fp8_prepare(desc: Desc, q, k, v, ops: "Fp8Operands" = None, stream=None) -> "Fp8Operands":
+    """FP8 operands (E4M3 codes and scales, V-Smooth means) of q, k, v (bf16 [B,H,N,d])."""
+    lib = load_library()
+    shp = (desc.B, desc.H, desc.N, desc.d)
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, name, shp, torch.bfloat16)
+    if ops is None:
+        ops = Fp8Operands(desc, q.device)
+    cd = desc.c()
+    rc = lib.ab_fp8_prepare(ctypes.byref(cd), _ptr(q), _ptr(k), _ptr(v), _ptr(ops.qcode), _ptr(ops.qscale),
+                            _ptr(ops.kcode), _ptr(ops.kscale), _ptr(ops.vcode), _ptr(ops.vmean), _ptr(ops.vscale),
+                            _ptr(ops.vmean_scaled), _ptr(ops.ws), ops.ws.numel() * 4, _stream(stream))
+    _check(rc, "ab_fp8_prepare")
+    return ops

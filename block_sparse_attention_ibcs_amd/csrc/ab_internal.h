@@ -77,4 +77,10 @@ hipError_t launch_attn_fwd(const Dims& D, const void* q, const void* k, const vo
                            const float* weights, const int32_t* counts, void* out, float* lse,
                            hipStream_t s);
 
+// FP8 variant: operand preparation (workspace: fp8_ws_bytes)
+size_t fp8_ws_bytes(const Dims& D);
+hipError_t launch_fp8_prepare(const Dims& D, const void* q, const void* k, const void* v, uint8_t* qcode,
+                              float* qscale, uint8_t* kcode, float* kscale, uint8_t* vcode, uint16_t* vmean,
+                              float* vscale, uint32_t* vmean_scaled, void* ws, hipStream_t s);
+
 }  // namespace ab

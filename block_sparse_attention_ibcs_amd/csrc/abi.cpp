@@ -239,4 +239,32 @@ int32_t ab_attn_fwd(const ab_desc* desc, const void* q, const void* k, const voi
   return AB_OK;
 }
 
+size_t ab_fp8_workspace_size(const ab_desc* desc) {
+  ab::Dims P;
+  if (make_dims(desc, &P) != AB_OK) return 0;
+  return ab::fp8_ws_bytes(P);
+}
+
+int32_t ab_fp8_prepare(const ab_desc* desc, const void* q, const void* k, const void* v, uint8_t* qcode,
+                       float* qscale, uint8_t* kcode, float* kscale, uint8_t* vcode, uint16_t* vmean,
+                       float* vscale, uint32_t* vmean_scaled, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  ab::Dims P;
+  int32_t rc = make_dims(desc, &P);
+  if (rc) return rc;
+  if (!P.bf16) return fail(AB_ERR_DTYPE, "the FP8 variant takes bf16 inputs");
+  if (!q || !k || !v || !qcode || !qscale || !kcode || !kscale || !vcode || !vmean || !vscale || !vmean_scaled || !ws)
+    return fail(AB_ERR_NULL, "every pointer of ab_fp8_prepare must be non-NULL");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(qcode, 16) || !aligned(kcode, 16) ||
+      !aligned(vcode, 16) || !aligned(vmean_scaled, 16) || !aligned(ws, 16))
+    return fail(AB_ERR_SHAPE, "q, k, v, qcode, kcode, vcode, vmean_scaled and ws must be 16-byte aligned");
+  const size_t need = ab::fp8_ws_bytes(P);
+  if (ws_bytes < need) return fail(AB_ERR_WORKSPACE, "workspace of %zu bytes < required %zu", ws_bytes, need);
+  if ((rc = check_device())) return rc;
+  hipError_t e = ab::launch_fp8_prepare(P, q, k, v, qcode, qscale, kcode, kscale, vcode, vmean, vscale, vmean_scaled,
+                                        ws, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "fp8 prepare launch");
+  return AB_OK;
+}
+
 }  // extern "C"

@@ -203,6 +203,41 @@ int32_t ab_attn_fwd(const ab_desc* desc, const void* q, const void* k, const voi
                     const int32_t* idx, const float* weights, const int32_t* counts,
                     void* out, float* lse, void* stream);
 
+/*
+ * ---- FP8 variant (VC-Attention page, iitak.ru news on MiniMax-H3: the attention
+ * products in 8-bit floating point, V-Smooth and ExpCast-FP8) ----
+ *
+ * Bytes of device workspace ab_fp8_prepare needs (per-sub-block and per-head
+ * residual maxima), or 0 when the descriptor is invalid.
+ */
+size_t ab_fp8_workspace_size(const ab_desc* desc);
+
+/*
+ * FP8 operands of one layer for ab_attn_fwd_fp8. Codes are OCP E4M3 (1 sign, 4
+ * exponent bits with bias 7, 3 mantissa bits, largest finite 448), rounded to
+ * nearest even from fp32, with one fp32 scale per block: the block's largest
+ * magnitude amax maps to 448, inv = 448/amax and scale = amax/448 both correctly
+ * rounded, code = E4M3(x * inv); an all-zero block has scale 0 and codes 0.
+ *
+ * desc:     dtype must be AB_BF16 (else AB_ERR_DTYPE).
+ * q, k, v:  device bf16 [B, H, N, d].
+ * qcode:    device uint8 [B, H, N, d], one scale per query block -> qscale fp32 [B, H, NQB].
+ * kcode:    device uint8 [B, H, N, d], one scale per key sub-block -> kscale fp32 [B, H, NKB].
+ * vmean:    device bf16 [B, H, NKB, d]: V-Smooth mean of each key sub-block (fp32 sum
+ *           of its real keys in ascending order, one division, rounded to bf16).
+ * vcode:    device uint8 [B, H, NKB, 2, d, k_block/2]: residual v - vmean of each key
+ *           quantised with one scale per head (vscale fp32 [B, H]); key t of a
+ *           sub-block sits at [(t >> 2) & 1][dim][(t >> 3) * 4 + (t & 3)] (the
+ *           operand order of the attention kernel); keys at or past N hold 0.
+ * vmean_scaled: device uint32 [B, H, NKB, d]: vmean / vscale (1 when vscale is 0)
+ *           as two bf16 halves, low 16 bits hi = bf16(x), high 16 bits lo = bf16(x - hi).
+ * ws:       device workspace of ws_bytes >= ab_fp8_workspace_size(desc), 16-byte aligned.
+ * q, k, v, qcode, kcode, vcode, vmean_scaled and ws must be 16-byte aligned.
+ */
+int32_t ab_fp8_prepare(const ab_desc* desc, const void* q, const void* k, const void* v, uint8_t* qcode,
+                       float* qscale, uint8_t* kcode, float* kscale, uint8_t* vcode, uint16_t* vmean,
+                       float* vscale, uint32_t* vmean_scaled, void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
