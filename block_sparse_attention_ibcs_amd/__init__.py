@@ -39,6 +39,7 @@ __all__ = [
     "EXPORTED_SYMBOLS",
     "Fp8Operands",
     "ab_fp8_prepare",
+    "ab_attn_fwd_fp8",
 ]
 
 AB_BF16 = 0
@@ -56,6 +57,7 @@ EXPORTED_SYMBOLS = (
     "ab_attn_fwd",
     "ab_fp8_workspace_size",
     "ab_fp8_prepare",
+    "ab_attn_fwd_fp8",
 )
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -158,6 +160,8 @@ def load_library():
     lib.ab_fp8_workspace_size.argtypes = [D]
     lib.ab_fp8_prepare.restype = ctypes.c_int32
     lib.ab_fp8_prepare.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.ab_attn_fwd_fp8.restype = ctypes.c_int32
+    lib.ab_attn_fwd_fp8.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, P, P]
     _lib = lib
     return lib
 
@@ -363,3 +367,24 @@ def ab_fp8_prepare(desc: Desc, q, k, v, ops: "Fp8Operands" = None, stream=None) 
                             _ptr(ops.vmean_scaled), _ptr(ops.ws), ops.ws.numel() * 4, _stream(stream))
     _check(rc, "ab_fp8_prepare")
     return ops
+
+
+def ab_attn_fwd_fp8(desc: Desc, ops: "Fp8Operands", idx, weights, counts, out=None, lse=None, want_lse=True,
+                    stream=None):
+    """FP8 weighted block-sparse attention from ab_fp8_prepare's operands; (out bf16, lse fp32 or None)."""
+    lib = load_library()
+    rows = (desc.B, desc.H, desc.nqb)
+    _need(idx, "idx", rows + (desc.nkb,), torch.int32)
+    _need(weights, "weights", rows + (desc.nkb,), torch.float32)
+    _need(counts, "counts", rows, torch.int32)
+    dev = ops.qcode.device
+    if out is None:
+        out = torch.empty((desc.B, desc.H, desc.N, desc.d), dtype=torch.bfloat16, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((desc.B, desc.H, desc.N), dtype=torch.float32, device=dev)
+    cd = desc.c()
+    rc = lib.ab_attn_fwd_fp8(ctypes.byref(cd), _ptr(ops.qcode), _ptr(ops.qscale), _ptr(ops.kcode), _ptr(ops.kscale),
+                             _ptr(ops.vcode), _ptr(ops.vscale), _ptr(ops.vmean_scaled), _ptr(idx), _ptr(weights),
+                             _ptr(counts), _ptr(out), _ptr(lse), _stream(stream))
+    _check(rc, "ab_attn_fwd_fp8")
+    return out, lse

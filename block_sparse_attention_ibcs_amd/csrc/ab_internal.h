@@ -82,5 +82,10 @@ size_t fp8_ws_bytes(const Dims& D);
 hipError_t launch_fp8_prepare(const Dims& D, const void* q, const void* k, const void* v, uint8_t* qcode,
                               float* qscale, uint8_t* kcode, float* kscale, uint8_t* vcode, uint16_t* vmean,
                               float* vscale, uint32_t* vmean_scaled, void* ws, hipStream_t s);
+// FP8 variant: attention (head dim 128, query block 128)
+hipError_t launch_attn_fwd_fp8(const Dims& D, const uint8_t* qcode, const float* qscale, const uint8_t* kcode,
+                               const float* kscale, const uint8_t* vcode, const float* vscale,
+                               const uint32_t* vmean_scaled, const int32_t* idx, const float* weights,
+                               const int32_t* counts, void* out, float* lse, hipStream_t s);
 
 }  // namespace ab

@@ -267,4 +267,25 @@ int32_t ab_fp8_prepare(const ab_desc* desc, const void* q, const void* k, const 
   return AB_OK;
 }
 
+int32_t ab_attn_fwd_fp8(const ab_desc* desc, const uint8_t* qcode, const float* qscale, const uint8_t* kcode,
+                        const float* kscale, const uint8_t* vcode, const float* vscale, const uint32_t* vmean_scaled,
+                        const int32_t* idx, const float* weights, const int32_t* counts, void* out, float* lse,
+                        void* stream) {
+  g_err[0] = 0;
+  ab::Dims P;
+  int32_t rc = make_dims(desc, &P);
+  if (rc) return rc;
+  if (!P.bf16) return fail(AB_ERR_DTYPE, "the FP8 variant takes bf16 inputs and writes bf16 output");
+  if (P.d != 128 || P.Bq != 128) return fail(AB_ERR_PARAM, "the FP8 attention takes d = 128 and q_block = 128 (got %d, %d)", P.d, P.Bq);
+  if (!qcode || !qscale || !kcode || !kscale || !vcode || !vscale || !vmean_scaled || !idx || !weights || !counts || !out)
+    return fail(AB_ERR_NULL, "every pointer of ab_attn_fwd_fp8 except lse must be non-NULL");
+  if (!aligned(qcode, 16) || !aligned(kcode, 16) || !aligned(vcode, 16) || !aligned(vmean_scaled, 16) || !aligned(out, 16))
+    return fail(AB_ERR_SHAPE, "qcode, kcode, vcode, vmean_scaled and out must be 16-byte aligned");
+  if ((rc = check_device())) return rc;
+  hipError_t e = ab::launch_attn_fwd_fp8(P, qcode, qscale, kcode, kscale, vcode, vscale, vmean_scaled, idx, weights,
+                                         counts, out, lse, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "fp8 attention launch");
+  return AB_OK;
+}
+
 }  // extern "C"

@@ -238,6 +238,28 @@ int32_t ab_fp8_prepare(const ab_desc* desc, const void* q, const void* k, const 
                        float* qscale, uint8_t* kcode, float* kscale, uint8_t* vcode, uint16_t* vmean,
                        float* vscale, uint32_t* vmean_scaled, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * FP8 weighted block-sparse attention (VC-Attention page: 8-bit products,
+ * V-Smooth add-back, ExpCast-FP8 probabilities) on the kept sub-blocks of
+ * ab_sample, from the operands of ab_fp8_prepare. Head dim 128 and q_block 128
+ * only (else AB_ERR_PARAM); k_block any of 16, 32, 64, 128.
+ *
+ * The kept sub-blocks of each query block are laid end to end and walked in
+ * 64-slot tiles; per tile and query row (log2 units):
+ *   x = qscale_i * kscale_j * scale * log2(e) * (qcode . kcode) + log2(w_j),
+ *   m <- max(m, max_tile x)  (O and l rescaled by 2^(m_old - m) when m moves),
+ *   p = E4M3 value of code = clamp(round_half_even(8 (x - m) + 126), 0, 126),
+ *   l += sum p,  O += vscale * sum p decode(vcode) + sum_t (sum of p over sub-block t) vmean_t;
+ * out = O / l (0 for an empty list), lse = (m + log2 l - 8.75) ln 2 (-inf if empty).
+ * idx, weights, counts: as written by ab_sample. out: device bf16 [B, H, N, 128];
+ * lse: device fp32 [B, H, N] or NULL. qcode, kcode, vcode, vmean_scaled and out
+ * must be 16-byte aligned.
+ */
+int32_t ab_attn_fwd_fp8(const ab_desc* desc, const uint8_t* qcode, const float* qscale, const uint8_t* kcode,
+                        const float* kscale, const uint8_t* vcode, const float* vscale, const uint32_t* vmean_scaled,
+                        const int32_t* idx, const float* weights, const int32_t* counts, void* out, float* lse,
+                        void* stream);
+
 #ifdef __cplusplus
 }
 #endif
