@@ -41,16 +41,20 @@ template <int D>
 __global__ __launch_bounds__(256) void quant_rows(int N, int rows_per, int nblk, const uint16_t* __restrict__ x,
                                                   uint8_t* __restrict__ codes, float* __restrict__ scales) {
   __shared__ float red[4];
+  constexpr int kMaxChunks = 128 * D / 8 / 256;  // 16-byte chunks per thread for up to 128 rows
   const int blk = blockIdx.x;
   const int i = blk % nblk, bh = blk / nblk;
   const int r0 = i * rows_per, r1 = min(N, r0 + rows_per);
   const size_t base = (size_t(bh) * N + r0) * D;
   const int n8 = (r1 - r0) * D / 8;  // 8-element (16-byte) chunks
   const uint4* src = reinterpret_cast<const uint4*>(x + base);
+  uint4 u[kMaxChunks];  // the block is read once and kept in registers
   float m = 0.0f;
-  for (int c = threadIdx.x; c < n8; c += blockDim.x) {
-    const uint4 u = src[c];
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int k = 0; k < kMaxChunks; ++k) {
+    const int c = threadIdx.x + k * 256;
+    u[k] = c < n8 ? src[c] : make_uint4(0, 0, 0, 0);
+    const uint32_t w[4] = {u[k].x, u[k].y, u[k].z, u[k].w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       m = fmaxf(m, fabsf(__uint_as_float(w[e] << 16)));
@@ -60,42 +64,55 @@ __global__ __launch_bounds__(256) void quant_rows(int N, int rows_per, int nblk,
   const float amax = block_max(m, red);
   const float inv = amax > 0.0f ? __fdiv_rn(kE4M3Max, amax) : 0.0f;
   uint2* dst = reinterpret_cast<uint2*>(codes + base);
-  for (int c = threadIdx.x; c < n8; c += blockDim.x) {
-    const uint4 u = src[c];
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-    uint32_t out[2] = {0u, 0u};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t lo = fp8_code(__fmul_rn(__uint_as_float(w[e] << 16), inv));
-      const uint32_t hi = fp8_code(__fmul_rn(__uint_as_float(w[e] & 0xFFFF0000u), inv));
-      out[e >> 1] |= (lo | (hi << 8)) << (16 * (e & 1));
+  for (int k = 0; k < kMaxChunks; ++k) {
+    const int c = threadIdx.x + k * 256;
+    if (c < n8) {
+      const uint32_t w[4] = {u[k].x, u[k].y, u[k].z, u[k].w};
+      uint32_t out[2] = {0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t lo = fp8_code(__fmul_rn(__uint_as_float(w[e] << 16), inv));
+        const uint32_t hi = fp8_code(__fmul_rn(__uint_as_float(w[e] & 0xFFFF0000u), inv));
+        out[e >> 1] |= (lo | (hi << 8)) << (16 * (e & 1));
+      }
+      dst[c] = make_uint2(out[0], out[1]);
     }
-    dst[c] = make_uint2(out[0], out[1]);
   }
   if (threadIdx.x == 0) scales[blk] = __fdiv_rn(amax, kE4M3Max);
 }
 
 // V-Smooth statistics of one key sub-block: per dimension the mean (fp32 sum in
 // ascending key order, one division, bf16) and the largest residual magnitude.
-// One thread per dimension.
-template <int D>
-__global__ __launch_bounds__(D) void v_stats(int N, int Bk, int nkb, const uint16_t* __restrict__ v,
-                                             uint16_t* __restrict__ vmean, float* __restrict__ ramax) {
+// The sub-block is staged in LDS with 16-byte loads; one thread per dimension sums
+// its column in key order.
+template <int D, int Bk>
+__global__ __launch_bounds__(256) void v_stats(int N, int nkb, const uint16_t* __restrict__ v,
+                                               uint16_t* __restrict__ vmean, float* __restrict__ ramax) {
+  __shared__ __align__(16) uint16_t tile[Bk * D];
+  __shared__ float mu[D];
   __shared__ float red[4];
   const int blk = blockIdx.x;
   const int j = blk % nkb, bh = blk / nkb;
-  const int r0 = j * Bk, r1 = min(N, r0 + Bk);
-  const int c = threadIdx.x;
-  const uint16_t* col = v + (size_t(bh) * N + r0) * D + c;
-  float s = 0.0f;
-  for (int r = 0; r < r1 - r0; ++r) s = __fadd_rn(s, bf16_to_f32(col[size_t(r) * D]));
-  const uint16_t mb = f32_to_bf16(__fdiv_rn(s, float(r1 - r0)));
-  vmean[size_t(blk) * D + c] = mb;
-  const float mu = bf16_to_f32(mb);
+  const int r0 = j * Bk, rows = min(N, r0 + Bk) - r0;
+  const uint4* src = reinterpret_cast<const uint4*>(v + (size_t(bh) * N + r0) * D);
+  uint4* dst = reinterpret_cast<uint4*>(tile);
+  for (int c = threadIdx.x; c < rows * D / 8; c += blockDim.x) dst[c] = src[c];
+  __syncthreads();
+  if (threadIdx.x < D) {
+    const int c = threadIdx.x;
+    float s = 0.0f;
+    for (int r = 0; r < rows; ++r) s = __fadd_rn(s, bf16_to_f32(tile[r * D + c]));
+    const uint16_t mb = f32_to_bf16(__fdiv_rn(s, float(rows)));
+    vmean[size_t(blk) * D + c] = mb;
+    mu[c] = bf16_to_f32(mb);
+  }
+  __syncthreads();
   float m = 0.0f;
-  for (int r = 0; r < r1 - r0; ++r) m = fmaxf(m, fabsf(__fsub_rn(bf16_to_f32(col[size_t(r) * D]), mu)));
+  for (int e = threadIdx.x; e < rows * D; e += blockDim.x)
+    m = fmaxf(m, fabsf(__fsub_rn(bf16_to_f32(tile[e]), mu[e % D])));
   const float bm = block_max(m, red);
-  if (c == 0) ramax[blk] = bm;
+  if (threadIdx.x == 0) ramax[blk] = bm;
 }
 
 // Per head: the residual scale from the sub-blocks' largest residuals.
@@ -114,16 +131,20 @@ __global__ __launch_bounds__(256) void v_scale(int nkb, const float* __restrict_
 
 // Residual codes of one sub-block in the operand layout, and the sub-block mean
 // divided by the head's residual scale (1 when the scale is 0) as a bf16 pair
-// (hi | lo << 16, hi + lo the fp32 quotient to about 2^-16).
-// Thread -> (group g of 4 keys, half h2, dimension d), dimension fastest.
-template <int D>
-__global__ __launch_bounds__(256) void v_codes(int N, int Bk, int nkb, const uint16_t* __restrict__ v,
+// (hi | lo << 16, hi + lo the fp32 quotient to about 2^-16). The sub-block is
+// staged in LDS; thread -> (group g of 4 keys, half h2, dimension d), dimension fastest.
+template <int D, int Bk>
+__global__ __launch_bounds__(256) void v_codes(int N, int nkb, const uint16_t* __restrict__ v,
                                                const uint16_t* __restrict__ vmean, const float* __restrict__ vscale,
                                                const float* __restrict__ hamax, uint8_t* __restrict__ vcode,
                                                uint32_t* __restrict__ vms) {
+  __shared__ __align__(16) uint16_t tile[Bk * D];
   const int blk = blockIdx.x;
   const int j = blk % nkb, bh = blk / nkb;
-  const int r0 = j * Bk;
+  const int r0 = j * Bk, rows = min(N, r0 + Bk) - r0;
+  const uint4* src = reinterpret_cast<const uint4*>(v + (size_t(bh) * N + r0) * D);
+  uint4* dst = reinterpret_cast<uint4*>(tile);
+  for (int c = threadIdx.x; c < rows * D / 8; c += blockDim.x) dst[c] = src[c];
   const float amax = hamax[bh];
   const float inv = amax > 0.0f ? __fdiv_rn(kE4M3Max, amax) : 0.0f;
   const float vs = vscale[bh] > 0.0f ? vscale[bh] : 1.0f;
@@ -134,8 +155,9 @@ __global__ __launch_bounds__(256) void v_codes(int N, int Bk, int nkb, const uin
     const uint16_t lo = f32_to_bf16(__fsub_rn(q, bf16_to_f32(hi)));
     vms[size_t(blk) * D + d] = uint32_t(hi) | (uint32_t(lo) << 16);
   }
-  const int groups = Bk / 8;  // 4-key groups per half
-  const int total = groups * 2 * D;
+  __syncthreads();
+  constexpr int groups = Bk / 8;  // 4-key groups per half
+  constexpr int total = groups * 2 * D;
   uint8_t* out = vcode + size_t(blk) * D * Bk;
   for (int p = threadIdx.x; p < total; p += blockDim.x) {
     const int d = p % D, h2 = (p / D) % 2, g = p / (2 * D);
@@ -144,12 +166,8 @@ __global__ __launch_bounds__(256) void v_codes(int N, int Bk, int nkb, const uin
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int t = g * 8 + h2 * 4 + e;  // key of the sub-block
-      const int r = r0 + t;
       uint32_t code = 0;
-      if (r < N) {
-        const float res = __fsub_rn(bf16_to_f32(v[(size_t(bh) * N + r) * D + d]), mu);
-        code = fp8_code(__fmul_rn(res, inv));
-      }
+      if (t < rows) code = fp8_code(__fmul_rn(__fsub_rn(bf16_to_f32(tile[t * D + d]), mu), inv));
       word |= code << (8 * e);
     }
     *reinterpret_cast<uint32_t*>(out + (size_t(h2) * D + d) * (Bk / 2) + g * 4) = word;
@@ -159,6 +177,31 @@ __global__ __launch_bounds__(256) void v_codes(int N, int Bk, int nkb, const uin
 }  // namespace
 
 size_t fp8_ws_bytes(const Dims& P) { return size_t(P.B) * P.H * (size_t(P.nkb) + 1) * sizeof(float); }
+
+namespace {
+
+template <int D, int Bk>
+void launch_v(const Dims& P, const uint16_t* V, uint16_t* vmean, float* vscale, uint8_t* vcode, uint32_t* vms,
+              float* ramax, float* hamax, hipStream_t s) {
+  const int heads = P.B * P.H;
+  hipLaunchKernelGGL((v_stats<D, Bk>), dim3(heads * P.nkb), dim3(256), 0, s, P.N, P.nkb, V, vmean, ramax);
+  hipLaunchKernelGGL(v_scale, dim3(heads), dim3(256), 0, s, P.nkb, ramax, vscale, hamax);
+  hipLaunchKernelGGL((v_codes<D, Bk>), dim3(heads * P.nkb), dim3(256), 0, s, P.N, P.nkb, V, vmean, vscale, hamax,
+                     vcode, vms);
+}
+
+template <int D>
+void launch_v_d(const Dims& P, const uint16_t* V, uint16_t* vmean, float* vscale, uint8_t* vcode, uint32_t* vms,
+                float* ramax, float* hamax, hipStream_t s) {
+  switch (P.Bk) {
+    case 16: launch_v<D, 16>(P, V, vmean, vscale, vcode, vms, ramax, hamax, s); break;
+    case 32: launch_v<D, 32>(P, V, vmean, vscale, vcode, vms, ramax, hamax, s); break;
+    case 64: launch_v<D, 64>(P, V, vmean, vscale, vcode, vms, ramax, hamax, s); break;
+    default: launch_v<D, 128>(P, V, vmean, vscale, vcode, vms, ramax, hamax, s); break;
+  }
+}
+
+}  // namespace
 
 hipError_t launch_fp8_prepare(const Dims& P, const void* q, const void* k, const void* v, uint8_t* qcode,
                               float* qscale, uint8_t* kcode, float* kscale, uint8_t* vcode, uint16_t* vmean,
@@ -172,17 +215,11 @@ hipError_t launch_fp8_prepare(const Dims& P, const void* q, const void* k, const
   if (P.d == 128) {
     hipLaunchKernelGGL(quant_rows<128>, dim3(heads * P.nqb), dim3(256), 0, s, P.N, P.Bq, P.nqb, Q, qcode, qscale);
     hipLaunchKernelGGL(quant_rows<128>, dim3(heads * P.nkb), dim3(256), 0, s, P.N, P.Bk, P.nkb, K, kcode, kscale);
-    hipLaunchKernelGGL(v_stats<128>, dim3(heads * P.nkb), dim3(128), 0, s, P.N, P.Bk, P.nkb, V, vmean, ramax);
-    hipLaunchKernelGGL(v_scale, dim3(heads), dim3(256), 0, s, P.nkb, ramax, vscale, hamax);
-    hipLaunchKernelGGL(v_codes<128>, dim3(heads * P.nkb), dim3(256), 0, s, P.N, P.Bk, P.nkb, V, vmean, vscale, hamax,
-                       vcode, vms);
+    launch_v_d<128>(P, V, vmean, vscale, vcode, vms, ramax, hamax, s);
   } else {
     hipLaunchKernelGGL(quant_rows<64>, dim3(heads * P.nqb), dim3(256), 0, s, P.N, P.Bq, P.nqb, Q, qcode, qscale);
     hipLaunchKernelGGL(quant_rows<64>, dim3(heads * P.nkb), dim3(256), 0, s, P.N, P.Bk, P.nkb, K, kcode, kscale);
-    hipLaunchKernelGGL(v_stats<64>, dim3(heads * P.nkb), dim3(64), 0, s, P.N, P.Bk, P.nkb, V, vmean, ramax);
-    hipLaunchKernelGGL(v_scale, dim3(heads), dim3(256), 0, s, P.nkb, ramax, vscale, hamax);
-    hipLaunchKernelGGL(v_codes<64>, dim3(heads * P.nkb), dim3(256), 0, s, P.N, P.Bk, P.nkb, V, vmean, vscale, hamax,
-                       vcode, vms);
+    launch_v_d<64>(P, V, vmean, vscale, vcode, vms, ramax, hamax, s);
   }
   return hipGetLastError();
 }
