@@ -28,6 +28,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak (published)
+PEAK_FP8_TFLOPS = 5000.0  # MI355X dense fp8 matrix-core peak (published)
 METRIC = "dense-equivalent attention TFLOP/s and ms/layer at ~10% density, 1 MI355X"
 ATTN_SOURCE = os.path.join(ROOT, "block_sparse_attention_ibcs_amd", "csrc", "attn_fwd.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_wan1.3b_traffic.txt")
@@ -44,6 +45,9 @@ def parse_args():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="wall time budget of the CPU oracle sample")
+    ap.add_argument("--fp8", action="store_true",
+                    help="run the FP8 variant of the attention stage (ab_fp8_prepare + ab_attn_fwd_fp8: E4M3 "
+                         "products, V-Smooth, ExpCast-FP8) instead of the bf16 kernel; not the headline line")
     ap.add_argument("--graph", action="store_true",
                     help="replay one step captured in a HIP graph instead of launching the three calls eagerly "
                          "(measured: no faster, the launches already run ahead of the GPU)")
@@ -367,6 +371,13 @@ def main():
 
     stream = torch.cuda.current_stream()
     ev = {name: [] for name in ("score", "sample", "attn")}
+    fp8_ops = None
+    if args.fp8:
+        if w.dtype != "bf16" or w.d != 128 or w.q_block != 128:
+            print("--fp8 needs a bf16 workload with d = 128 and q_block = 128", file=sys.stderr)
+            sys.exit(2)
+        fp8_ops = ab.Fp8Operands(desc, dev)
+        ev["fp8_prepare"] = []
 
     def step(record=False):
         e = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if record else None
@@ -378,12 +389,26 @@ def main():
         ab.ab_sample(desc, scores, density, args.seed, idx=idx, weights=wts, counts=cnt, want_mask=False)
         if record:
             e[2].record(stream)
-        ab.ab_attn_fwd(desc, qd, kd, vd, idx, wts, cnt, out=out, lse=lse)
+        if fp8_ops is None:
+            ab.ab_attn_fwd(desc, qd, kd, vd, idx, wts, cnt, out=out, lse=lse)
+            if record:
+                e[3].record(stream)
+        else:
+            ab.ab_fp8_prepare(desc, qd, kd, vd, ops=fp8_ops)
+            if record:
+                e.append(torch.cuda.Event(enable_timing=True))
+                e[3].record(stream)
+            ab.ab_attn_fwd_fp8(desc, fp8_ops, idx, wts, cnt, out=out, lse=lse)
+            if record:
+                e[4].record(stream)
         if record:
-            e[3].record(stream)
             ev["score"].append((e[0], e[1]))
             ev["sample"].append((e[1], e[2]))
-            ev["attn"].append((e[2], e[3]))
+            if fp8_ops is None:
+                ev["attn"].append((e[2], e[3]))
+            else:
+                ev["fp8_prepare"].append((e[2], e[3]))
+                ev["attn"].append((e[3], e[4]))
 
     # One step captured in a HIP graph (the same kernels on the same buffers, launched as
     # one graph): the timed loop replays it. The path issues no memsets, so the graph
@@ -422,7 +447,16 @@ def main():
 
     attn_s = stage_ms["attn"] / 1e3
     achieved = actual_flops / attn_s / 1e12
-    traffic = read_traffic(args.workload)
+    traffic = read_traffic(args.workload) if fp8_ops is None else None
+    peak = PEAK_BF16_TFLOPS if fp8_ops is None else PEAK_FP8_TFLOPS
+    fp8_vs_bf16 = None
+    if fp8_ops is not None:
+        # accuracy of the FP8 variant: relative L2 distance of its output from the bf16
+        # kernel's on the same kept lists (the bf16 path is within ~0.3% of exact)
+        ref, _ = ab.ab_attn_fwd(desc, qd, kd, vd, idx, wts, cnt, want_lse=False)
+        torch.cuda.synchronize()
+        fp8_vs_bf16 = float(torch.linalg.vector_norm((out.float() - ref.float()).flatten()) /
+                            torch.linalg.vector_norm(ref.float().flatten()))
     result = {
         "metric": METRIC,
         "value": dense / (ms_per_step / 1e3) / 1e12,
@@ -434,7 +468,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "dtype": ("bf16" if w.dtype == "bf16" else "f32") if fp8_ops is None else "fp8-e4m3 (attention products)",
         "data": "synthetic (seeded smooth 3D positional field + noise; no model weights)",
         "config": {
             "workload": f"{args.workload}: B={w.B} H={w.H} grid={'x'.join(map(str, w.grid))} N={w.N} d={w.d} "
@@ -445,24 +479,26 @@ def main():
             "realised_density": realised,
             "stage_ms": stage_ms,
             "hip_graph": bool(args.graph),
+            "attention_variant": "bf16" if fp8_ops is None else "fp8 (E4M3 QK and PV, V-Smooth, ExpCast-FP8)",
+            "fp8_rel_l2_vs_bf16_path": fp8_vs_bf16,
             "attn_actual_tflops": achieved,
             "attn_dense_equivalent_tflops": dense / attn_s / 1e12,
             "layer_actual_tflops_excl_scorer": actual_flops / (ms_per_step / 1e3) / 1e12,
         },
         "roofline": {
-            "kernel": "attn_fwd_bf16",
+            "kernel": "attn_fwd_bf16" if fp8_ops is None else "attn_fwd_fp8",
             "bound": "mfma",
             "achieved": achieved,
-            "peak": PEAK_BF16_TFLOPS,
+            "peak": peak,
             "unit": "TFLOP/s",
-            "frac": achieved / PEAK_BF16_TFLOPS,
+            "frac": achieved / peak,
             "traffic": traffic,
             "flops_per_launch": actual_flops,
             "launch_ms": stage_ms["attn"],
         },
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and fp8_ops is None:
         result["cpu_baseline"] = cpu_baseline(w, q, k, v, density, args.seed, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
