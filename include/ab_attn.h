@@ -95,10 +95,13 @@ size_t ab_score_workspace_size(const ab_desc* desc);
  * IBCS block-importance estimates (AB-Attention abstract, IBCS sentence).
  *
  * For each query block (b, h, i): k-means with C clusters and T iterations on
- * the block's queries (exact-operation fp32: left-to-right distance sums with
- * separate multiply and add, ties to the lowest cluster, members summed in
- * ascending row order, one correctly rounded division; strided initial
- * centroids; empty clusters keep their centroid with size 0), then
+ * the block's queries (exact-operation fp32: a query is compared with centroid
+ * mu through |mu|^2 - 2 x.mu, i.e. |mu|^2 then one fused multiply-add of
+ * x_k * (-2 mu_k) per dimension in ascending order, |mu|^2 being rounded
+ * products summed by a halving tree within each group of 64 dimensions and the
+ * groups added in order; ties to the lowest cluster; members summed in ascending
+ * row order, one correctly rounded division; strided initial centroids; empty
+ * clusters keep their centroid with size 0), then
  *   scores[b,h,i,j] = sum_c (n_c/n_i) * exp(l_cj - L_c),
  *   l_cj = log sum_{k in sub-block j} exp(scale * mu_c . k_k),  L_c = log sum_j exp(l_cj),
  * with mu_c rounded to bf16 before the product for bf16 inputs. Each score row

@@ -14,11 +14,16 @@ algorithm nor the estimate's formula. Readings used here:
   centroid by the mean of its members; an empty cluster keeps its centroid and
   gets size 0.
 * It is specified operation by operation in fp32 so that any correct
-  implementation reproduces it bit for bit: a distance is the left-to-right
-  fp32 sum over dimensions of fl(fl(x - mu)^2) starting from 0 with separate
-  multiply and add (no fused multiply-add); a centroid is the fp32 sum of its
-  members in ascending row order, divided by the member count with one
-  correctly rounded fp32 division.
+  implementation reproduces it bit for bit. Queries are compared through
+  |mu_c|^2 - 2 x.mu_c, the squared distance less the query's own |x|^2, which
+  leaves the nearest centroid unchanged: starting from |mu_c|^2, each dimension
+  k in ascending order adds x_k * (-2 mu_ck) with one fused multiply-add
+  (-2 mu is exact). |mu_c|^2 rounds each product mu_k^2 to fp32 and sums them
+  within each group of 64 dimensions by the halving tree (k with k+32, then k
+  with k+16, ..., then k with k+1; absent dimensions count as 0), then adds
+  the group sums left to right. A centroid is the fp32 sum of its members in
+  ascending row order, divided by the member count with one correctly rounded
+  fp32 division.
 * Each cluster stands in for its members by its centroid. For bf16 inputs the
   centroid is rounded to bf16 (ties to even) before it meets the keys, since
   that is the precision the keys have.
@@ -37,6 +42,68 @@ def round_bf16(x):
     lsb = (u >> np.uint64(16)) & np.uint64(1)
     r = ((u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)) << np.uint64(16)
     return (r & np.uint64(0xFFFFFFFF)).astype(np.uint32).view(np.float32).reshape(np.shape(x))
+
+
+def fma_f32(a, b, c):
+    """fp32 fused multiply-add a*b + c with a single rounding (nearest, ties to even).
+
+    The product of two fp32 values is exact in float64 (at most 48 significant
+    bits). The float64 sum p + c is made exact-or-odd: its rounding error e comes
+    from Knuth's TwoSum, and an inexact sum whose last bit is even is moved one
+    float64 step towards the exact value. Rounding to odd with two or more spare
+    bits, then to nearest at the narrower precision, gives the correctly rounded
+    result (Boldo and Melquiond, "Emulation of FMA and correctly rounded sums:
+    proved algorithms using rounding to odd", IEEE Trans. Computers, 2008).
+    """
+    a64 = np.asarray(a, dtype=np.float32).astype(np.float64)
+    b64 = np.asarray(b, dtype=np.float32).astype(np.float64)
+    c64 = np.asarray(c, dtype=np.float32).astype(np.float64)
+    p = a64 * b64
+    with np.errstate(invalid="ignore", over="ignore"):
+        s = p + c64
+        bv = s - p
+        e = (p - (s - bv)) + (c64 - bv)
+        s = np.array(s, dtype=np.float64, copy=True)
+        even = (s.view(np.int64) & 1) == 0
+        fix = np.isfinite(s) & (e != 0) & even
+        if np.any(fix):
+            s[fix] = np.nextafter(s[fix], np.where(e[fix] > 0, np.inf, -np.inf))
+        return s.astype(np.float32)
+
+
+def centroid_sqnorm(mu):
+    """|mu|^2 over the last axis, as the clustering computes it (fp32).
+
+    Products rounded one by one; halving-tree sum inside each group of 64
+    dimensions (zero-padded); group sums added left to right.
+    """
+    mu = np.asarray(mu, dtype=np.float32)
+    d = mu.shape[-1]
+    G = -(-d // 64)
+    t = np.zeros(mu.shape[:-1] + (G * 64,), dtype=np.float32)
+    t[..., :d] = mu * mu
+    t = t.reshape(mu.shape[:-1] + (G, 64))
+    for s in (32, 16, 8, 4, 2, 1):
+        t[..., :s] = t[..., :s] + t[..., s:2 * s]
+    out = t[..., 0, 0].copy()
+    for g in range(1, G):
+        out = out + t[..., g, 0]
+    return out
+
+
+def kmeans_distances(X, mu):
+    """Comparison distances |mu_c|^2 - 2 x_r.mu_c, fp32 [..., n, C].
+
+    X: float32 [..., n, d]; mu: float32 [..., C, d]. Each entry starts at the
+    centroid's norm and takes one fused multiply-add per dimension, ascending.
+    """
+    X = np.asarray(X, dtype=np.float32)
+    mu = np.asarray(mu, dtype=np.float32)
+    m2 = (np.float32(-2.0) * mu).astype(np.float32)
+    D = np.broadcast_to(centroid_sqnorm(mu)[..., None, :], X.shape[:-1] + (mu.shape[-2],)).astype(np.float32)
+    for k in range(X.shape[-1]):
+        D = fma_f32(X[..., :, None, k], m2[..., None, :, k], D)
+    return D
 
 
 def kmeans_fp32(X, n_clusters, iters, return_history=False):
@@ -66,14 +133,12 @@ def kmeans_fp32(X, n_clusters, iters, return_history=False):
     assign = np.zeros((nb, n), dtype=np.int64)
     history = []
     for _ in range(T):
-        # assignment: D(r, c) = (((0 + e_0) + e_1) + ...) with e_k = fl(fl(x_k - mu_k)^2)
-        D = np.zeros((nb, n, Ci), dtype=np.float32)
-        for k in range(d):
-            diff = X[:, :, None, k] - mu[:, None, :Ci, k]
-            D = D + diff * diff
+        # assignment: nearest centroid by |mu|^2 - 2 x.mu
+        D = kmeans_distances(X, mu[:, :Ci])
         assign = np.argmin(D, axis=2)  # first minimum, i.e. lowest cluster index on ties
         if return_history:
-            history.append(float(np.take_along_axis(D, assign[:, :, None], 2).astype(np.float64).sum()))
+            diff = X.astype(np.float64) - np.take_along_axis(mu[:, :Ci], assign[:, :, None], 1).astype(np.float64)
+            history.append(float((diff * diff).sum()))
         # update: members summed in ascending row order, one division per coordinate
         sums = np.zeros((nb, Ci, d), dtype=np.float32)
         counts = np.zeros((nb, Ci), dtype=np.int64)

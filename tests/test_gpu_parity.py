@@ -458,19 +458,20 @@ def test_sampler_rows_any_length(nkb, density):
 
 @pytest.mark.parametrize("dim", [64, 128])
 def test_kmeans_rounding_case(dim):
-    """A block where a fused multiply-add in the distance would flip one assignment:
-    the GPU clustering must match the oracle bit for bit there too."""
+    """A block (fp32 queries) where separately rounded multiplies and adds in the
+    comparison would flip one assignment: the GPU clustering must match the oracle
+    bit for bit there too."""
     _gpu()
     import kmeans_rounding_case as case
 
-    X, row, separate, fused = case.build(dim)
+    X, row, fused, separate = case.build(dim)
     n = X.shape[0]
-    desc = ab.Desc(1, 1, n, dim, ab.AB_BF16, 64, 16, 2, kmeans_iters=1)
-    q = torch.from_numpy(X).to(torch.bfloat16).reshape(1, 1, n, dim).cuda()
+    desc = ab.Desc(1, 1, n, dim, ab.AB_F32, 64, 16, 2, kmeans_iters=1)
+    q = torch.from_numpy(X).reshape(1, 1, n, dim).cuda()
     cent, sizes, assign = ab.ab_score_debug(desc, q)
     torch.cuda.synchronize()
     mu, sz, asg = kmeans_fp32(X, 2, 1)
-    assert int(asg[row]) == separate != fused
+    assert int(asg[row]) == fused != separate
     assert np.array_equal(assign.cpu().numpy()[0, 0], asg.astype(np.uint8))
     assert np.array_equal(sizes.cpu().numpy()[0, 0, 0], sz)
     assert np.array_equal(cent.cpu().numpy()[0, 0, 0].view(np.uint32), mu.view(np.uint32))

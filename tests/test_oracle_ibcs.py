@@ -9,6 +9,12 @@
   are taken; the result matches scikit-learn's Lloyd iterations from the same
   initial centroids.
 * Score rows sum to 1, and bf16 rounding matches torch's.
+* The clustering's fp32 arithmetic: the fused multiply-add against hand-worked
+  values (one where separate rounding gives 0, one where rounding the float64
+  sum directly to fp32 rounds twice) and against exact rationals; the centroid
+  norm's halving tree and the comparison distances against exact-rational
+  step-by-step evaluation; a block where only fused arithmetic gives the
+  oracle's assignment.
 """
 
 import math
@@ -17,7 +23,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle.ibcs import block_scores, kmeans_fp32, round_bf16
+from oracle.ibcs import block_scores, centroid_sqnorm, fma_f32, kmeans_distances, kmeans_fp32, round_bf16
 
 
 def _dense_block_mass(q, k, k_block, scale):
@@ -98,13 +104,18 @@ def test_p4_kmeans_invariants():
         # objective non-increasing across iterations (exact arithmetic; fp32 slack)
         for a, b in zip(hist, hist[1:]):
             assert b <= a * (1 + 1e-5) + 1e-6
-        # the last assignment is nearest-centroid w.r.t. the centroids before the final update
-        mu_prev, _, assign_prev = kmeans_fp32(X, C, T - 1)[:3] if T > 1 else (None, None, None)
+        # the last assignment is nearest-centroid w.r.t. the centroids before the final
+        # update, up to the rounding of the fp32 comparison: each compared value is an
+        # fp32 chain of d fused multiply-adds plus a norm of at most d + 7 rounded
+        # steps, so its error is below (2d + 8) u (|mu|^2 + 2 sum |x mu|), u = 2^-24
         if T > 1:
-            D = ((X.astype(np.float64)[:, None, :] - mu_prev.astype(np.float64)[None, :Ci, :]) ** 2).sum(axis=2)
-            best = D.min(axis=1)
-            chosen = D[np.arange(n), assign]
-            assert np.all(chosen <= best * (1 + 1e-5) + 1e-6)
+            mu_prev = kmeans_fp32(X, C, T - 1)[0].astype(np.float64)[:Ci]
+            X64 = X.astype(np.float64)
+            D = ((X64[:, None, :] - mu_prev[None, :, :]) ** 2).sum(axis=2)
+            bound = (2 * d + 8) * 2.0 ** -24 * ((mu_prev ** 2).sum(axis=1)[None, :] + 2 * np.abs(X64) @ np.abs(mu_prev).T)
+            best = D.argmin(axis=1)
+            rows = np.arange(n)
+            assert np.all(D[rows, assign] <= D[rows, best] + bound[rows, assign] + bound[rows, best])
         # T matters: one more iteration changes nothing only if converged
         mu2, _, assign2 = kmeans_fp32(X, C, T + 1)
         if not np.array_equal(assign2, assign):
@@ -150,15 +161,75 @@ def test_bf16_rounding_matches_torch():
     np.testing.assert_array_equal(round_bf16(x), ref)
 
 
-@pytest.mark.parametrize("dim", [64, 128])
-def test_kmeans_rounds_multiply_and_add_separately(dim):
-    """On a block built so that one row's two distances are equal in exact arithmetic,
-    the oracle's assignment is the one of separately rounded multiplies and adds
-    (computed here term by term) and not the one of a fused multiply-add (computed
-    with exact rationals): the spec's rounding is what decides it."""
+def test_fma_f32_hand_worked():
+    a = np.float32(1 + 2.0 ** -12)  # a*a = 1 + 2^-11 + 2^-24 exactly
+    # separate rounding loses the 2^-24 (a tie at 1 + 2^-11, kept even), the fused form keeps it
+    assert fma_f32(a, a, np.float32(-(1 + 2.0 ** -11))) == np.float32(2.0 ** -24)
+    assert np.float32(np.float32(a * a) - np.float32(1 + 2.0 ** -11)) == 0.0
+    # exact value 1 + 2^-11 + 2^-24 + 2^-80 lies just above the fp32 midpoint: correct
+    # rounding goes up; the float64 sum is the midpoint itself and would round down to even
+    got = fma_f32(a, a, np.float32(2.0 ** -80))
+    assert got == np.float32(1 + 2.0 ** -11 + 2.0 ** -23)
+    assert np.float32(np.float64(a) * np.float64(a) + 2.0 ** -80) == np.float32(1 + 2.0 ** -11)
+    # same below the midpoint: the exact value rounds down
+    assert fma_f32(a, a, np.float32(-(2.0 ** -80))) == np.float32(1 + 2.0 ** -11)
+    # signs, zero and an exact result
+    assert fma_f32(np.float32(-3.0), np.float32(0.5), np.float32(1.5)) == 0.0
+    assert fma_f32(np.float32(2.0), np.float32(3.0), np.float32(-1.0)) == np.float32(5.0)
+
+
+def test_fma_f32_against_exact_rationals():
     import kmeans_rounding_case as case
 
-    X, row, separate, fused = case.build(dim)
-    assert separate != fused
+    rng = np.random.default_rng(21)
+    n = 3000
+    a = (rng.standard_normal(n) * 2.0 ** rng.integers(-20, 20, n)).astype(np.float32)
+    b = (rng.standard_normal(n) * 2.0 ** rng.integers(-20, 20, n)).astype(np.float32)
+    c = (rng.standard_normal(n) * 2.0 ** rng.integers(-40, 40, n)).astype(np.float32)
+    # a third of the cases cancel the product almost exactly, where rounding matters most
+    k = n // 3
+    c[:k] = (-(a[:k].astype(np.float64) * b[:k].astype(np.float64))).astype(np.float32)
+    got = fma_f32(a, b, c)
+    for i in range(n):
+        assert got[i] == case.fma_exact(a[i], b[i], c[i]), (a[i], b[i], c[i])
+
+
+@pytest.mark.parametrize("d", [8, 64, 100, 128])
+def test_centroid_sqnorm_tree(d):
+    import kmeans_rounding_case as case
+
+    rng = np.random.default_rng(d)
+    mu = (rng.standard_normal((3, d)) * 10.0 ** rng.uniform(-2, 2, size=(3, d))).astype(np.float32)
+    got = centroid_sqnorm(mu)
+    for c in range(3):
+        assert got[c] == case.sqnorm_exact(mu[c])
+        np.testing.assert_allclose(float(got[c]), float((mu[c].astype(np.float64) ** 2).sum()), rtol=1e-5)
+
+
+@pytest.mark.parametrize("d", [16, 70])
+def test_kmeans_distances_stepwise(d):
+    import kmeans_rounding_case as case
+
+    rng = np.random.default_rng(100 + d)
+    X = rng.standard_normal((6, d)).astype(np.float32)
+    mu = (rng.standard_normal((3, d)) + 0.5).astype(np.float32)
+    D = kmeans_distances(X, mu)
+    for r in range(6):
+        for c in range(3):
+            assert D[r, c] == case.distance_fused(X[r], mu[c])
+    # and it is the squared distance less |x|^2, up to rounding
+    ref = ((X.astype(np.float64)[:, None, :] - mu.astype(np.float64)[None]) ** 2).sum(-1) - (X.astype(np.float64) ** 2).sum(-1)[:, None]
+    np.testing.assert_allclose(D, ref, rtol=0, atol=1e-4 * (1 + np.abs(ref).max()))
+
+
+@pytest.mark.parametrize("dim", [64, 128])
+def test_kmeans_distance_uses_fused_multiply_add(dim):
+    """On a block built so that one row's two comparisons are equal in exact arithmetic,
+    the oracle's assignment is the one of the fused chain and not the one of separately
+    rounded multiplies and adds (both computed with exact rationals)."""
+    import kmeans_rounding_case as case
+
+    X, row, fused, separate = case.build(dim)
+    assert fused != separate
     _, _, assign = kmeans_fp32(X, 2, 1)
-    assert int(assign[row]) == separate
+    assert int(assign[row]) == fused
