@@ -30,8 +30,13 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak (published)
 PEAK_FP8_TFLOPS = 5000.0  # MI355X dense fp8 matrix-core peak (published)
 METRIC = "dense-equivalent attention TFLOP/s and ms/layer at ~10% density, 1 MI355X"
-ATTN_SOURCE = os.path.join(ROOT, "block_sparse_attention_ibcs_amd", "csrc", "attn_fwd.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_wan1.3b_traffic.txt")
+# committed HBM-counter summary and kernel source of each attention variant
+TRAFFIC = {
+    "bf16": (os.path.join(ROOT, "profiles", "attn_fwd_wan1.3b_traffic.txt"),
+             os.path.join(ROOT, "block_sparse_attention_ibcs_amd", "csrc", "attn_fwd.hip")),
+    "fp8": (os.path.join(ROOT, "profiles", "attn_fp8_wan1.3b_traffic.txt"),
+            os.path.join(ROOT, "block_sparse_attention_ibcs_amd", "csrc", "attn_fp8.hip")),
+}
 
 
 def parse_args():
@@ -64,22 +69,24 @@ def parse_args():
     return ap.parse_args()
 
 
-def attn_source_digest():
-    with open(ATTN_SOURCE, "rb") as f:
+def source_digest(path):
+    with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def read_traffic(workload):
-    """HBM bytes per attention launch from the committed counter summary, if it matches the current kernel."""
-    if not os.path.exists(TRAFFIC_FILE):
+def read_traffic(workload, variant):
+    """HBM bytes per attention launch from the committed counter summary, if it was
+    taken on this workload with the current kernel source; else None."""
+    summary, source = TRAFFIC[variant]
+    if not os.path.exists(summary):
         return None
     vals = {}
-    with open(TRAFFIC_FILE) as f:
+    with open(summary) as f:
         for line in f:
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 vals[k.strip()] = v.strip()
-    if vals.get("kernel_source_sha256_16") != attn_source_digest() or vals.get("workload") != workload:
+    if vals.get("kernel_source_sha256_16") != source_digest(source) or vals.get("workload") != workload:
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])
@@ -447,7 +454,7 @@ def main():
 
     attn_s = stage_ms["attn"] / 1e3
     achieved = actual_flops / attn_s / 1e12
-    traffic = read_traffic(args.workload) if fp8_ops is None else None
+    traffic = read_traffic(args.workload, "bf16" if fp8_ops is None else "fp8")
     peak = PEAK_BF16_TFLOPS if fp8_ops is None else PEAK_FP8_TFLOPS
     fp8_vs_bf16 = None
     if fp8_ops is not None:
