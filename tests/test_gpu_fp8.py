@@ -6,6 +6,8 @@ scaled-mean pairs): each is a fixed sequence of correctly rounded fp32 operation
 and one E4M3 rounding, computed the same way on both sides.
 """
 
+import functools
+
 import numpy as np
 import pytest
 import torch
@@ -81,11 +83,19 @@ def test_prepare_head_dim_64_and_zero_blocks():
     _check_prepare(q, k, v, 64, 32)
 
 
-def test_prepare_video_shape_two_heads():
-    w = workloads.get("wan1.3b")
+@functools.lru_cache(maxsize=2)
+def _two_heads(name):
+    """The workload's first and last head at full sequence length, as bf16 CPU tensors."""
+    w = workloads.get(name)
     q, k, v = workloads.generate(w, seed=0)
     sel = [0, w.H - 1]
-    q, k, v = (torch.from_numpy(np.ascontiguousarray(x[:, sel])).to(torch.bfloat16) for x in (q, k, v))
+    return tuple(torch.from_numpy(np.ascontiguousarray(x[:, sel])).to(torch.bfloat16) for x in (q, k, v))
+
+
+@pytest.mark.parametrize("name", ["wan1.3b", "hunyuan"])
+def test_prepare_video_shape_two_heads(name):
+    w = workloads.get(name)
+    q, k, v = _two_heads(name)
     _check_prepare(q, k, v, w.q_block, w.k_block)
 
 
@@ -180,10 +190,13 @@ def test_attn_fp8_dense_and_peaked():
     _check_attn(q, k, v, 32, 1.0, seed=7)
 
 
-def test_attn_fp8_video_shape():
-    w = workloads.get("wan1.3b")
-    q, k, v = workloads.generate(w, seed=0)
-    q, k, v = (torch.from_numpy(x).to(torch.bfloat16) for x in (q, k, v))
+@pytest.mark.parametrize("name", ["wan1.3b", "hunyuan"])
+def test_attn_fp8_video_shape(name):
+    """Full sequence length of the workload (its first and last head), sampled blocks
+    and rows: the wan1.3b shape (k_block 32, 1024 sub-blocks a row) and the
+    HunyuanVideo shape (k_block 16, 7425 sub-blocks a row, ragged tail)."""
+    w = workloads.get(name)
+    q, k, v = _two_heads(name)
     nqb = -(-w.N // w.q_block)
-    blocks = [(0, 0, 0), (0, 0, nqb - 1), (0, w.H - 1, 77), (0, w.H - 1, nqb - 1)]
+    blocks = [(0, 0, 0), (0, 0, nqb - 1), (0, 1, 77), (0, 1, nqb - 1)]
     _check_attn(q, k, v, w.k_block, w.density, seed=11, blocks=blocks, rows_per_block=6)
