@@ -154,3 +154,49 @@ def test_python_binding_rejects_host_tensors():
     q = torch.zeros(1, 1, 256, 64)
     with pytest.raises(ValueError):
         ab.ab_score(d, q, q, workspace=torch.zeros(16, dtype=torch.uint8))
+
+
+def test_fp8_workspace_and_validation():
+    """FP8 entry points: workspace size (one fp32 per head and key sub-block plus one
+    per head), and every argument error caught before any device work."""
+    lib = _lib()
+    cd = _desc().c()
+    need = lib.ab_fp8_workspace_size(ctypes.byref(cd))
+    assert need == 1 * 12 * (1024 + 1) * 4
+    assert lib.ab_fp8_workspace_size(ctypes.byref(_desc(d=96).c())) == 0
+    fake = ctypes.c_void_p(256)
+    odd = ctypes.c_void_p(256 + 8)
+
+    def prep(desc, ptrs=None, ws_bytes=need):
+        p = ptrs or [fake] * 12  # q k v qcode qscale kcode kscale vcode vmean vscale vmean_scaled ws
+        return lib.ab_fp8_prepare(ctypes.byref(desc), *p[:12], ws_bytes, None)
+
+    assert prep(_desc(dtype=ab.AB_F32).c()) == -5
+    assert prep(_desc(d=96).c()) == -2
+    for i in range(12):
+        p = [fake] * 12
+        p[i] = None
+        assert prep(cd, p) == -1, i
+    for i in (0, 1, 2, 3, 5, 7, 10, 11):  # the 16-byte aligned operands
+        p = [fake] * 12
+        p[i] = odd
+        assert prep(cd, p) == -2, i
+    assert prep(cd, ws_bytes=need - 1) == -6
+    assert b"workspace" in lib.ab_last_error()
+
+    def attn(desc, ptrs=None):
+        p = ptrs or [fake] * 12  # qcode qscale kcode kscale vcode vscale vmean_scaled idx weights counts out lse
+        return lib.ab_attn_fwd_fp8(ctypes.byref(desc), *p, None)
+
+    assert attn(_desc(dtype=ab.AB_F32).c()) == -5
+    assert attn(_desc(d=64).c()) == -3
+    assert attn(_desc(q_block=64).c()) == -3
+    assert b"d = 128" in lib.ab_last_error()
+    for i in range(11):  # every pointer but lse is required
+        p = [fake] * 12
+        p[i] = None
+        assert attn(cd, p) == -1, i
+    for i in (0, 2, 4, 6, 10):
+        p = [fake] * 12
+        p[i] = odd
+        assert attn(cd, p) == -2, i
