@@ -330,7 +330,8 @@ def main():
     args = parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path is single-GPU by design "
-              "(heads shard across GPUs with no exchange, see DESIGN.md).", file=sys.stderr)
+              "(on several GPUs the heads would be split between them, each GPU running the whole path "
+              "on its heads with no exchange).", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
