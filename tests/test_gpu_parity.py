@@ -600,3 +600,63 @@ def test_injected_index_lists_bf16():
                                            1 / math.sqrt(d))
         assert np.all(np.abs(out[0, 0, lo:hi] - o_ref) <= o_bound(o_ref, TOL["bf16"]))
         assert np.abs(lse[0, 0, lo:hi] - l_ref).max() <= 1e-3 * max(1.0, np.abs(l_ref).max())
+
+
+def _seed_means(desc, qd, kd, vd, density, seeds, unit_weights=False):
+    """Per-row means and standard errors over sampling seeds of the weighted estimate's
+    denominator exp(LSE) and numerator O exp(LSE), both relative to the dense
+    denominator, from the GPU sampler and attention kernel (scores computed once).
+    unit_weights: the same draws with every weight 1 (plain truncation)."""
+    q64, k64, v64 = (x[0, 0].float().cpu().numpy() for x in (qd, kd, vd))
+    o_dense, lse_dense = dense_attention(q64, k64, v64, 1.0 / math.sqrt(desc.d))
+    scores = ab.ab_score(desc, qd, kd)
+    acc = {n: 0.0 for n in ("num", "num2", "den", "den2")}
+    for seed in range(seeds):
+        idx, wts, cnt, _ = ab.ab_sample(desc, scores, density, seed, want_mask=False)
+        if unit_weights:
+            wts = torch.ones_like(wts)
+        out, lse = ab.ab_attn_fwd(desc, qd, kd, vd, idx, wts, cnt)
+        den = np.exp(lse[0, 0].cpu().numpy().astype(np.float64) - lse_dense)
+        num = out[0, 0].float().cpu().numpy().astype(np.float64) * den[:, None]
+        acc["num"] = acc["num"] + num
+        acc["num2"] = acc["num2"] + num * num
+        acc["den"] = acc["den"] + den
+        acc["den2"] = acc["den2"] + den * den
+    mean = {n: acc[n] / seeds for n in ("num", "den")}
+    se = {n: np.sqrt(np.maximum(acc[n + "2"] / seeds - mean[n] ** 2, 0.0) / seeds) for n in ("num", "den")}
+    return mean, se, o_dense
+
+
+@pytest.mark.parametrize("case", ["tiny-fp32", "bf16-d128"])
+def test_gpu_estimate_is_unbiased(case):
+    """SIP sentence: sampling in proportion to the scores and reweighting by the inverse
+    inclusion probability makes one pass an unbiased estimate of dense attention. The
+    GPU path's numerator and denominator, averaged over sampling seeds, lie within five
+    standard errors of exact dense attention (float64 on the CPU)."""
+    dev = _gpu()
+    if case == "tiny-fp32":
+        w = workloads.get("tiny")
+        q, k, v = workloads.generate(w, seed=0)
+        qd, kd, vd = (torch.from_numpy(x).to(dev) for x in (q, k, v))
+        desc = ab.Desc.for_tensor(qd, w.q_block, w.k_block, w.n_clusters, w.kmeans_iters)
+        density, seeds, tol = 0.25, 1000, 1e-6
+    else:
+        g = torch.Generator().manual_seed(5)
+        base = torch.randn((1, 1, 1000, 128), generator=g)
+        qd = (base + 0.5 * torch.randn((1, 1, 1000, 128), generator=g)).to(torch.bfloat16).to(dev)
+        kd = (base + 0.5 * torch.randn((1, 1, 1000, 128), generator=g)).to(torch.bfloat16).to(dev)
+        vd = torch.randn((1, 1, 1000, 128), generator=g).to(torch.bfloat16).to(dev)
+        desc = ab.Desc.for_tensor(qd, 128, 16, 8)
+        # the kernel's bf16 probabilities and output add a deterministic error of up to
+        # about 2^-8 relative on top of the sampling noise
+        density, seeds, tol = 0.2, 300, 2.0 ** -8
+    mean, se, o_dense = _seed_means(desc, qd, kd, vd, density, seeds)
+    assert np.all(np.abs(mean["den"] - 1.0) <= 5 * se["den"] + tol)
+    scale = np.abs(o_dense).max()
+    assert np.all(np.abs(mean["num"] - o_dense) <= 5 * se["num"] + tol * scale)
+    # the estimate is not trivially exact: the seeds do differ
+    assert se["den"].max() > 0
+    # and the check has power: without the inverse-probability weights the same draws
+    # underestimate the denominator far beyond five standard errors
+    mean1, se1, _ = _seed_means(desc, qd, kd, vd, density, seeds // 4, unit_weights=True)
+    assert np.mean(np.abs(mean1["den"] - 1.0) > 5 * se1["den"] + tol) > 0.5
