@@ -13,6 +13,10 @@ reweighted by the inverse inclusion probability so one pass estimates dense
 attention (SIP sentence). The pages give no formulas; every constant and rule
 the abstract leaves open is a stated reading, listed in the module that uses it.
 
+The INTRA relay patterns (``intra``) follow the INTRA page (paperdot search page,
+query "Wenbo Lu"): static Scatter / Gather kept lists under a partition model,
+an alternative index producer for the same weighted attention.
+
 The FP8 variant (``fp8``) follows the VC-Attention page (iitak.ru news on
 MiniMax-H3): 8-bit products, V-Smooth (per-block mean subtracted, residual
 quantised) and ExpCast-FP8 (the FP8 byte of a probability from one linear
@@ -34,6 +38,7 @@ from .systematic import sample_rows_systematic
 from .attention import dense_attention, sparse_ht_attention
 from .pipeline import Params, run_blocks
 from . import fp8
+from . import intra
 
 __all__ = [
     "philox4x32_10",
