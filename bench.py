@@ -56,6 +56,8 @@ def parse_args():
     ap.add_argument("--graph", action="store_true",
                     help="replay one step captured in a HIP graph instead of launching the three calls eagerly "
                          "(measured: no faster, the launches already run ahead of the GPU)")
+    ap.add_argument("--intra", action="store_true",
+                    help="INTRA Scatter/Gather patterns through the attention kernel on --workload; one JSON line per layer kind")
     ap.add_argument("--sweep", action="store_true",
                     help="gather-cost sweep on the 75600-token, 40-head shape: density {1, .25, .10, .05} x k_block "
                          "{16, 32, 64, 128}; one JSON line per point instead of the headline line")
@@ -197,6 +199,74 @@ def run_sweep(args):
             }), flush=True)
         del ws, scores, idx, wts, cnt, out, lse
         torch.cuda.empty_cache()
+
+
+def run_intra(args):
+    """INTRA relay patterns as a second index producer for the same attention kernel:
+    Scatter and Gather lists (ab_intra_lists, default neighbourhood of
+    q_block*ceil(sqrt(NQB)) tokens) on the workload's inputs; list generation and
+    attention timed with HIP events on their stream; one JSON line per layer kind."""
+    import numpy as np
+    import torch
+
+    import block_sparse_attention_ibcs_amd as ab
+    import workloads
+
+    w = workloads.get(args.workload)
+    if args.k_block:
+        w = w.with_(k_block=args.k_block)
+    q, k, v = workloads.generate(w, seed=0)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = (torch.from_numpy(x).to(torch.bfloat16).to(dev) for x in (q, k, v))
+    del q, k, v
+    stream = torch.cuda.current_stream()
+    desc = ab.Desc.for_tensor(qd, w.q_block, w.k_block, w.n_clusters, w.kmeans_iters)
+    nqb, nkb = desc.nqb, desc.nkb
+    rows = (w.B, w.H, nqb)
+    idx = torch.empty(rows + (nkb,), dtype=torch.int32, device=dev)
+    wts = torch.empty(rows + (nkb,), dtype=torch.float32, device=dev)
+    cnt = torch.empty(rows, dtype=torch.int32, device=dev)
+    out = torch.empty_like(qd)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    dense = w.dense_flops()
+    L = w.q_block * int(np.ceil(np.sqrt(nqb)))
+
+    def timed(fn, reps):
+        evs = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            evs.append((a, b))
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    for layer, name in ((ab.AB_INTRA_SCATTER, "scatter"), (ab.AB_INTRA_GATHER, "gather")):
+        list_fn = lambda: ab.ab_intra_lists(desc, layer, 0, idx=idx, weights=wts, counts=cnt)  # noqa: E731
+        attn_fn = lambda: ab.ab_attn_fwd(desc, qd, kd, vd, idx, wts, cnt, out=out, lse=lse)  # noqa: E731
+        list_fn()
+        attn_fn()
+        torch.cuda.synchronize()
+        flops, realised = attention_work(w, nqb, nkb, idx, cnt)
+        for _ in range(args.warmup):
+            attn_fn()
+        list_ms = timed(list_fn, args.steps)
+        attn_ms = timed(attn_fn, args.steps)
+        achieved = flops / (attn_ms / 1e3) / 1e12
+        print(json.dumps({
+            "intra_layer": name,
+            "workload": f"{w.name}: B={w.B} H={w.H} N={w.N} d={w.d} Bq={w.q_block} Bk={w.k_block}",
+            "neighbourhood_tokens": L,
+            "realised_density": realised,
+            "list_ms": list_ms,
+            "attn_ms": attn_ms,
+            "attn_actual_tflops": achieved,
+            "attn_mfma_frac": achieved / PEAK_BF16_TFLOPS,
+            "attn_flops": flops,
+            "attn_dense_equivalent_tflops": dense / (attn_ms / 1e3) / 1e12,
+            "steps": args.steps,
+        }), flush=True)
 
 
 ABLATION_DENSITIES = (0.05, 0.10, 0.25)
@@ -345,6 +415,9 @@ def main():
     ab.load_library()  # fails loudly if the HIP library is not built
     if args.sweep:
         run_sweep(args)
+        return
+    if args.intra:
+        run_intra(args)
         return
     if args.ablation:
         run_ablation(args)

@@ -10,6 +10,7 @@ Stages (AB-Attention abstract, paperdot search page, query "Xing Ma"):
   ab_sample    SIP draw with inverse-inclusion-probability weights
   ab_sample_systematic  fixed-size systematic draw with the same inclusion probabilities
   ab_sample_topk  top-K truncation of the same scores (weight 1; for estimator comparisons)
+  ab_intra_lists  INTRA's static Scatter / Gather relay patterns as kept lists (INTRA page)
   ab_attn_fwd  weighted block-sparse attention over the kept sub-blocks
 """
 
@@ -32,8 +33,11 @@ __all__ = [
     "ab_sample",
     "ab_sample_systematic",
     "ab_sample_topk",
+    "ab_intra_lists",
     "ab_attn_fwd",
     "AbError",
+    "AB_INTRA_SCATTER",
+    "AB_INTRA_GATHER",
     "AB_BF16",
     "AB_F32",
     "EXPORTED_SYMBOLS",
@@ -44,6 +48,8 @@ __all__ = [
 
 AB_BF16 = 0
 AB_F32 = 1
+AB_INTRA_SCATTER = 0
+AB_INTRA_GATHER = 1
 EXPORTED_SYMBOLS = (
     "ab_abi_version",
     "ab_status_str",
@@ -54,6 +60,7 @@ EXPORTED_SYMBOLS = (
     "ab_sample",
     "ab_sample_systematic",
     "ab_sample_topk",
+    "ab_intra_lists",
     "ab_attn_fwd",
     "ab_fp8_workspace_size",
     "ab_fp8_prepare",
@@ -154,6 +161,8 @@ def load_library():
     lib.ab_sample_systematic.argtypes = [D, P, ctypes.c_double, ctypes.c_uint64, P, P, P, P, P]
     lib.ab_sample_topk.restype = ctypes.c_int32
     lib.ab_sample_topk.argtypes = [D, P, ctypes.c_double, P, P, P, P, P]
+    lib.ab_intra_lists.restype = ctypes.c_int32
+    lib.ab_intra_lists.argtypes = [D, ctypes.c_int32, ctypes.c_int32, P, P, P, P]
     lib.ab_attn_fwd.restype = ctypes.c_int32
     lib.ab_attn_fwd.argtypes = [D, P, P, P, P, P, P, P, P, P]
     lib.ab_fp8_workspace_size.restype = ctypes.c_size_t
@@ -308,6 +317,29 @@ def ab_sample_topk(desc: Desc, scores, density: float, idx=None, weights=None, c
                             _ptr(mask), _stream(stream))
     _check(rc, "ab_sample_topk")
     return idx, weights, counts, mask
+
+
+def ab_intra_lists(desc: Desc, layer: int, partition_tokens: int = 0, idx=None, weights=None, counts=None,
+                   device=None, stream=None):
+    """INTRA Scatter (layer 0) or Gather (layer 1) pattern: (idx int32, weights fp32 [B,H,NQB,NKB],
+    counts int32 [B,H,NQB]); partition_tokens 0 selects q_block * ceil(sqrt(NQB))."""
+    lib = load_library()
+    rows = (desc.B, desc.H, desc.nqb)
+    dev = device if device is not None else (idx.device if idx is not None else torch.device("cuda"))
+    if idx is None:
+        idx = torch.empty(rows + (desc.nkb,), dtype=torch.int32, device=dev)
+    if weights is None:
+        weights = torch.empty(rows + (desc.nkb,), dtype=torch.float32, device=dev)
+    if counts is None:
+        counts = torch.empty(rows, dtype=torch.int32, device=dev)
+    _need(idx, "idx", rows + (desc.nkb,), torch.int32)
+    _need(weights, "weights", rows + (desc.nkb,), torch.float32)
+    _need(counts, "counts", rows, torch.int32)
+    cd = desc.c()
+    rc = lib.ab_intra_lists(ctypes.byref(cd), int(layer), int(partition_tokens), _ptr(idx), _ptr(weights),
+                            _ptr(counts), _stream(stream))
+    _check(rc, "ab_intra_lists")
+    return idx, weights, counts
 
 
 def ab_attn_fwd(desc: Desc, q, k, v, idx, weights, counts, out=None, lse=None, want_lse=True, stream=None):

@@ -18,7 +18,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libabattn.so")
-SOURCES = ["kmeans.hip", "score.hip", "sample.hip", "attn_fwd.hip", "fp8_prep.hip", "attn_fp8.hip", "abi.cpp"]
+SOURCES = ["kmeans.hip", "score.hip", "sample.hip", "intra.hip", "attn_fwd.hip", "fp8_prep.hip", "attn_fp8.hip",
+           "abi.cpp"]
 
 ARCH = "gfx950"
 FLAGS = [

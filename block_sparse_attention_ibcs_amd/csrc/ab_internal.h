@@ -77,6 +77,11 @@ hipError_t launch_attn_fwd(const Dims& D, const void* q, const void* k, const vo
                            const float* weights, const int32_t* counts, void* out, float* lse,
                            hipStream_t s);
 
+// INTRA relay patterns: kept-sub-block lists of one layer (AB_INTRA_SCATTER or AB_INTRA_GATHER)
+hipError_t launch_intra_lists(const Dims& D, int layer, int partition_tokens, int32_t* idx, float* weights,
+                              int32_t* counts, hipStream_t s);
+int intra_default_partition(const Dims& D);  // q_block * ceil(sqrt(NQB))
+
 // FP8 variant: operand preparation (workspace: fp8_ws_bytes)
 size_t fp8_ws_bytes(const Dims& D);
 hipError_t launch_fp8_prepare(const Dims& D, const void* q, const void* k, const void* v, uint8_t* qcode,

@@ -223,6 +223,25 @@ int32_t ab_sample_topk(const ab_desc* desc, const float* scores, double density,
   return AB_OK;
 }
 
+int32_t ab_intra_lists(const ab_desc* desc, int32_t layer, int32_t partition_tokens, int32_t* idx, float* weights,
+                       int32_t* counts, void* stream) {
+  g_err[0] = 0;
+  ab::Dims P;
+  int32_t rc = make_dims(desc, &P);
+  if (rc) return rc;
+  if (layer != AB_INTRA_SCATTER && layer != AB_INTRA_GATHER)
+    return fail(AB_ERR_PARAM, "layer must be AB_INTRA_SCATTER or AB_INTRA_GATHER (got %d)", layer);
+  const int L = partition_tokens == 0 ? ab::intra_default_partition(P) : partition_tokens;
+  if (L < P.Bq || L % P.Bq != 0 || L > (1 << 30))
+    return fail(AB_ERR_PARAM, "partition_tokens must be 0 or a multiple of q_block in [q_block, 2^30] (got %d)",
+                partition_tokens);
+  if (!idx || !weights || !counts) return fail(AB_ERR_NULL, "idx, weights and counts must be non-NULL");
+  if ((rc = check_device())) return rc;
+  hipError_t e = ab::launch_intra_lists(P, layer, L, idx, weights, counts, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "INTRA list launch");
+  return AB_OK;
+}
+
 int32_t ab_attn_fwd(const ab_desc* desc, const void* q, const void* k, const void* v, const int32_t* idx,
                     const float* weights, const int32_t* counts, void* out, float* lse, void* stream) {
   g_err[0] = 0;

@@ -185,6 +185,33 @@ int32_t ab_sample_topk(const ab_desc* desc, const float* scores, double density,
                        float* weights, int32_t* counts, uint32_t* mask_bits, void* stream);
 
 /*
+ * INTRA relay patterns as kept-sub-block lists for ab_attn_fwd (INTRA page,
+ * paperdot search page, query "Wenbo Lu": static sparse attention over
+ * computational query sets, Scatter relay groups drawing on every local
+ * neighbourhood and Gather reconnecting them, under a partition model).
+ *
+ * The sequence is cut into neighbourhoods of L = partition_tokens tokens (0 selects
+ * q_block * ceil(sqrt(NQB))); query block i sits at offset o_i = (i * q_block) mod L
+ * of neighbourhood (i * q_block) / L.
+ *   AB_INTRA_SCATTER: the key sub-blocks at offsets [o_i, o_i + q_block) of every
+ *                     neighbourhood (those holding real tokens);
+ *   AB_INTRA_GATHER:  the key sub-blocks of query block i's own neighbourhood.
+ * Every kept sub-block gets weight 1 (exact attention over the pattern). The two
+ * layers in sequence connect every query token to every key token when L divides N.
+ *
+ * idx:      device int32 [B, H, NQB, NKB]: kept sub-blocks in ascending order, the
+ *           first counts[b,h,i] entries of each row written (the rest untouched).
+ * weights:  device fp32 [B, H, NQB, NKB]: 1.0 for the written entries.
+ * counts:   device int32 [B, H, NQB].
+ * Errors: AB_ERR_PARAM for another layer value or an L that is not a multiple of
+ * q_block in [q_block, 2^30]; AB_ERR_NULL for NULL outputs.
+ */
+#define AB_INTRA_SCATTER 0
+#define AB_INTRA_GATHER 1
+int32_t ab_intra_lists(const ab_desc* desc, int32_t layer, int32_t partition_tokens, int32_t* idx,
+                       float* weights, int32_t* counts, void* stream);
+
+/*
  * Weighted block-sparse attention forward (AB-Attention abstract, problem,
  * SIP and kernel sentences).
  *

@@ -200,3 +200,18 @@ def test_fp8_workspace_and_validation():
         p = [fake] * 12
         p[i] = odd
         assert attn(cd, p) == -2, i
+
+
+def test_intra_lists_validation():
+    """INTRA pattern lists: layer and neighbourhood-size checks, NULL outputs."""
+    lib = _lib()
+    cd = _desc().c()
+    fake = ctypes.c_void_p(256)
+    assert lib.ab_intra_lists(ctypes.byref(cd), 2, 0, fake, fake, fake, None) == -3
+    assert lib.ab_intra_lists(ctypes.byref(cd), -1, 0, fake, fake, fake, None) == -3
+    for L in (64, 192, -128, (1 << 30) + 128):  # below q_block, not a multiple of it, negative, too large
+        assert lib.ab_intra_lists(ctypes.byref(cd), 0, L, fake, fake, fake, None) == -3, L
+    assert b"partition_tokens" in lib.ab_last_error()
+    assert lib.ab_intra_lists(ctypes.byref(cd), 1, 2048, None, fake, fake, None) == -1
+    assert lib.ab_intra_lists(ctypes.byref(cd), 1, 0, fake, fake, None, None) == -1
+    assert lib.ab_intra_lists(ctypes.byref(_desc(q_block=32).c()), 0, 0, fake, fake, fake, None) == -3

@@ -26,6 +26,7 @@ import block_sparse_attention_ibcs_amd as ab
 import workloads
 from oracle import (Params, dense_attention, kmeans_fp32, block_scores, sample_rows, sample_rows_systematic,
                     sparse_ht_attention, topk_rows)
+from oracle.intra import default_partition, intra_lists
 from oracle.sip import SIP_ONE
 
 pytestmark = pytest.mark.gpu
@@ -660,3 +661,72 @@ def test_gpu_estimate_is_unbiased(case):
     # underestimate the denominator far beyond five standard errors
     mean1, se1, _ = _seed_means(desc, qd, kd, vd, density, seeds // 4, unit_weights=True)
     assert np.mean(np.abs(mean1["den"] - 1.0) > 5 * se1["den"] + tol) > 0.5
+
+
+class _IntraRun:
+    """GPU INTRA pattern lists (ab_intra_lists) and the attention over them, for check_attention."""
+
+    def __init__(self, w, inputs, layer, partition):
+        _gpu()
+        self.w = w
+        self.q, self.k, self.v = inputs
+        tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+        qd, kd, vd = (_to_dev(x, tdt) for x in (self.q, self.k, self.v))
+        self.desc = ab.Desc.for_tensor(qd, w.q_block, w.k_block, w.n_clusters, w.kmeans_iters)
+        self.scale = 1.0 / math.sqrt(w.d)
+        idx, wts, cnt = ab.ab_intra_lists(self.desc, layer, partition, device=qd.device)
+        out, lse = ab.ab_attn_fwd(self.desc, qd, kd, vd, idx, wts, cnt)
+        torch.cuda.synchronize()
+        self.idx, self.wts, self.cnt = idx.cpu().numpy(), wts.cpu().numpy(), cnt.cpu().numpy()
+        self.out, self.lse = out.float().cpu().numpy(), lse.cpu().numpy()
+
+
+def _check_intra_lists(run, layer, partition):
+    w = run.w
+    L = partition or default_partition(w.N, w.q_block)
+    ref_idx, ref_w, ref_cnt = intra_lists(w.N, w.q_block, w.k_block, L, "gather" if layer == ab.AB_INTRA_GATHER else "scatter")
+    for b in range(w.B):
+        for h in range(w.H):
+            assert np.array_equal(run.cnt[b, h], ref_cnt), (b, h)
+            for i in range(w.nqb):
+                c = ref_cnt[i]
+                assert np.array_equal(run.idx[b, h, i, :c], ref_idx[i, :c]), (b, h, i)
+                assert np.all(run.wts[b, h, i, :c] == 1.0), (b, h, i)
+
+
+INTRA_SHAPES = [
+    # (N, H, d, Bq, Bk, L); L = 0 selects q_block * ceil(sqrt(NQB))
+    (1000, 2, 128, 128, 32, 256),
+    (777, 1, 128, 128, 16, 384),
+    (520, 2, 64, 64, 16, 64),
+    (2048, 1, 128, 128, 64, 512),
+    (1000, 1, 128, 128, 128, 0),
+    (300, 1, 128, 128, 32, 512),  # one neighbourhood: Gather is dense, Scatter block-diagonal
+]
+
+
+@pytest.mark.parametrize("layer", [0, 1])
+@pytest.mark.parametrize("N,H,d,Bq,Bk,L", INTRA_SHAPES)
+def test_intra_patterns(N, H, d, Bq, Bk, L, layer):
+    """INTRA Scatter / Gather lists bit-exact against the oracle on every row, and the
+    attention over them against exact attention on those keys, every query block."""
+    w = workloads.Workload("intra", 1, H, (1, 1, N), d, "bf16", Bq, Bk, 8, 0.1, 0.5, False)
+    rng = np.random.default_rng(N + Bk + L)
+    base = rng.standard_normal((1, H, N, d)).astype(np.float32)
+    inputs = tuple(workloads.round_to_bf16(x) for x in (
+        base + 0.5 * rng.standard_normal((1, H, N, d)).astype(np.float32),
+        base + 0.5 * rng.standard_normal((1, H, N, d)).astype(np.float32),
+        rng.standard_normal((1, H, N, d)).astype(np.float32)))
+    run = _IntraRun(w, inputs, layer, L)
+    _check_intra_lists(run, layer, L)
+    check_attention(run, [(0, h, i) for h in range(H) for i in range(w.nqb)])
+
+
+@pytest.mark.parametrize("layer", [0, 1])
+def test_intra_video_shape(layer):
+    """The Wan2.1-1.3B shape (32760 tokens, 12 heads) with the default neighbourhood
+    (2048 tokens, a partial last one): lists on every row, attention on sampled blocks."""
+    w = workloads.get("wan1.3b")
+    run = _IntraRun(w, workloads.generate(w, seed=0), layer, 0)
+    _check_intra_lists(run, layer, 0)
+    check_attention(run, Run.blocks(run, max_blocks=12))
