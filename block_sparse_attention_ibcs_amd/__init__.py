@@ -35,6 +35,7 @@ __all__ = [
     "ab_sample_topk",
     "ab_intra_lists",
     "ab_attn_fwd",
+    "ab_attn_fwd_ordered",
     "AbError",
     "AB_INTRA_SCATTER",
     "AB_INTRA_GATHER",
@@ -62,6 +63,7 @@ EXPORTED_SYMBOLS = (
     "ab_sample_topk",
     "ab_intra_lists",
     "ab_attn_fwd",
+    "ab_attn_fwd_ordered",
     "ab_fp8_workspace_size",
     "ab_fp8_prepare",
     "ab_attn_fwd_fp8",
@@ -162,9 +164,11 @@ def load_library():
     lib.ab_sample_topk.restype = ctypes.c_int32
     lib.ab_sample_topk.argtypes = [D, P, ctypes.c_double, P, P, P, P, P]
     lib.ab_intra_lists.restype = ctypes.c_int32
-    lib.ab_intra_lists.argtypes = [D, ctypes.c_int32, ctypes.c_int32, P, P, P, P]
+    lib.ab_intra_lists.argtypes = [D, ctypes.c_int32, ctypes.c_int32, P, P, P, P, P]
     lib.ab_attn_fwd.restype = ctypes.c_int32
     lib.ab_attn_fwd.argtypes = [D, P, P, P, P, P, P, P, P, P]
+    lib.ab_attn_fwd_ordered.restype = ctypes.c_int32
+    lib.ab_attn_fwd_ordered.argtypes = [D, P, P, P, P, P, P, P, P, P, P]
     lib.ab_fp8_workspace_size.restype = ctypes.c_size_t
     lib.ab_fp8_workspace_size.argtypes = [D]
     lib.ab_fp8_prepare.restype = ctypes.c_int32
@@ -320,9 +324,10 @@ def ab_sample_topk(desc: Desc, scores, density: float, idx=None, weights=None, c
 
 
 def ab_intra_lists(desc: Desc, layer: int, partition_tokens: int = 0, idx=None, weights=None, counts=None,
-                   device=None, stream=None):
+                   row_order=None, want_order=False, device=None, stream=None):
     """INTRA Scatter (layer 0) or Gather (layer 1) pattern: (idx int32, weights fp32 [B,H,NQB,NKB],
-    counts int32 [B,H,NQB]); partition_tokens 0 selects q_block * ceil(sqrt(NQB))."""
+    counts int32 [B,H,NQB]), plus the processing order int32 [B*H*NQB] for ab_attn_fwd_ordered
+    when want_order (or row_order is given); partition_tokens 0 selects q_block * ceil(sqrt(NQB))."""
     lib = load_library()
     rows = (desc.B, desc.H, desc.nqb)
     dev = device if device is not None else (idx.device if idx is not None else torch.device("cuda"))
@@ -335,11 +340,15 @@ def ab_intra_lists(desc: Desc, layer: int, partition_tokens: int = 0, idx=None, 
     _need(idx, "idx", rows + (desc.nkb,), torch.int32)
     _need(weights, "weights", rows + (desc.nkb,), torch.float32)
     _need(counts, "counts", rows, torch.int32)
+    if row_order is None and want_order:
+        row_order = torch.empty(desc.B * desc.H * desc.nqb, dtype=torch.int32, device=dev)
+    if row_order is not None:
+        _need(row_order, "row_order", (desc.B * desc.H * desc.nqb,), torch.int32)
     cd = desc.c()
     rc = lib.ab_intra_lists(ctypes.byref(cd), int(layer), int(partition_tokens), _ptr(idx), _ptr(weights),
-                            _ptr(counts), _stream(stream))
+                            _ptr(counts), _ptr(row_order), _stream(stream))
     _check(rc, "ab_intra_lists")
-    return idx, weights, counts
+    return (idx, weights, counts, row_order) if row_order is not None else (idx, weights, counts)
 
 
 def ab_attn_fwd(desc: Desc, q, k, v, idx, weights, counts, out=None, lse=None, want_lse=True, stream=None):
@@ -360,6 +369,29 @@ def ab_attn_fwd(desc: Desc, q, k, v, idx, weights, counts, out=None, lse=None, w
     rc = lib.ab_attn_fwd(ctypes.byref(cd), _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(weights), _ptr(counts),
                          _ptr(out), _ptr(lse), _stream(stream))
     _check(rc, "ab_attn_fwd")
+    return out, lse
+
+
+def ab_attn_fwd_ordered(desc: Desc, q, k, v, idx, weights, counts, row_order, out=None, lse=None, want_lse=True,
+                        stream=None):
+    """ab_attn_fwd with the query-block rows taken in row_order (int32 [B*H*NQB]); same outputs."""
+    lib = load_library()
+    shp = (desc.B, desc.H, desc.N, desc.d)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, shp, desc.torch_dtype)
+    rows = (desc.B, desc.H, desc.nqb)
+    _need(idx, "idx", rows + (desc.nkb,), torch.int32)
+    _need(weights, "weights", rows + (desc.nkb,), torch.float32)
+    _need(counts, "counts", rows, torch.int32)
+    _need(row_order, "row_order", (desc.B * desc.H * desc.nqb,), torch.int32)
+    if out is None:
+        out = torch.empty(shp, dtype=desc.torch_dtype, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty(shp[:3], dtype=torch.float32, device=q.device)
+    cd = desc.c()
+    rc = lib.ab_attn_fwd_ordered(ctypes.byref(cd), _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(weights),
+                                 _ptr(counts), _ptr(row_order), _ptr(out), _ptr(lse), _stream(stream))
+    _check(rc, "ab_attn_fwd_ordered")
     return out, lse
 
 

@@ -73,13 +73,14 @@ hipError_t launch_sample(const Dims& D, const float* scores, int K, uint64_t see
 constexpr int kTopkMaxNkb = 16384;  // longest row the top-K and systematic kernels take
 hipError_t launch_topk(const Dims& D, const float* scores, int K, int32_t* idx, float* weights, int32_t* counts,
                        uint32_t* mask, hipStream_t s);
+// order: NULL, or the rows in the order the workgroups take them (rows outside the grid skipped)
 hipError_t launch_attn_fwd(const Dims& D, const void* q, const void* k, const void* v, const int32_t* idx,
                            const float* weights, const int32_t* counts, void* out, float* lse,
-                           hipStream_t s);
+                           const int32_t* order, hipStream_t s);
 
 // INTRA relay patterns: kept-sub-block lists of one layer (AB_INTRA_SCATTER or AB_INTRA_GATHER)
 hipError_t launch_intra_lists(const Dims& D, int layer, int partition_tokens, int32_t* idx, float* weights,
-                              int32_t* counts, hipStream_t s);
+                              int32_t* counts, int32_t* row_order, hipStream_t s);
 int intra_default_partition(const Dims& D);  // q_block * ceil(sqrt(NQB))
 
 // FP8 variant: operand preparation (workspace: fp8_ws_bytes)

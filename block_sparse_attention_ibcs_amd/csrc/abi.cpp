@@ -224,7 +224,7 @@ int32_t ab_sample_topk(const ab_desc* desc, const float* scores, double density,
 }
 
 int32_t ab_intra_lists(const ab_desc* desc, int32_t layer, int32_t partition_tokens, int32_t* idx, float* weights,
-                       int32_t* counts, void* stream) {
+                       int32_t* counts, int32_t* row_order, void* stream) {
   g_err[0] = 0;
   ab::Dims P;
   int32_t rc = make_dims(desc, &P);
@@ -237,7 +237,7 @@ int32_t ab_intra_lists(const ab_desc* desc, int32_t layer, int32_t partition_tok
                 partition_tokens);
   if (!idx || !weights || !counts) return fail(AB_ERR_NULL, "idx, weights and counts must be non-NULL");
   if ((rc = check_device())) return rc;
-  hipError_t e = ab::launch_intra_lists(P, layer, L, idx, weights, counts, static_cast<hipStream_t>(stream));
+  hipError_t e = ab::launch_intra_lists(P, layer, L, idx, weights, counts, row_order, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "INTRA list launch");
   return AB_OK;
 }
@@ -253,7 +253,25 @@ int32_t ab_attn_fwd(const ab_desc* desc, const void* q, const void* k, const voi
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
     return fail(AB_ERR_SHAPE, "q, k, v and out must be 16-byte aligned");
   if ((rc = check_device())) return rc;
-  hipError_t e = ab::launch_attn_fwd(P, q, k, v, idx, weights, counts, out, lse, static_cast<hipStream_t>(stream));
+  hipError_t e = ab::launch_attn_fwd(P, q, k, v, idx, weights, counts, out, lse, nullptr, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return AB_OK;
+}
+
+int32_t ab_attn_fwd_ordered(const ab_desc* desc, const void* q, const void* k, const void* v, const int32_t* idx,
+                            const float* weights, const int32_t* counts, const int32_t* row_order, void* out,
+                            float* lse, void* stream) {
+  g_err[0] = 0;
+  ab::Dims P;
+  int32_t rc = make_dims(desc, &P);
+  if (rc) return rc;
+  if (!q || !k || !v || !idx || !weights || !counts || !row_order || !out)
+    return fail(AB_ERR_NULL, "q, k, v, idx, weights, counts, row_order and out must be non-NULL");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
+    return fail(AB_ERR_SHAPE, "q, k, v and out must be 16-byte aligned");
+  if ((rc = check_device())) return rc;
+  hipError_t e = ab::launch_attn_fwd(P, q, k, v, idx, weights, counts, out, lse, row_order,
+                                     static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return AB_OK;
 }

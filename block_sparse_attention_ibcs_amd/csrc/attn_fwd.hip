@@ -74,7 +74,7 @@ __global__ __launch_bounds__(BQ * 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_bf16(Dims P, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                    const uint16_t* __restrict__ v, const int32_t* __restrict__ idx,
                    const float* __restrict__ weights, const int32_t* __restrict__ counts,
-                   uint16_t* __restrict__ out, float* __restrict__ lse) {
+                   uint16_t* __restrict__ out, float* __restrict__ lse, const int32_t* __restrict__ order) {
   using Cfg = AttnCfg<D, BQ, BK>;
   // Four separate LDS objects (K and V, two stages each): the compiler can then tell
   // that the gather landing in one stage does not alias the reads of the other, and
@@ -87,7 +87,11 @@ void attn_fwd_bf16(Dims P, const uint16_t* __restrict__ q, const uint16_t* __res
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, col = lane & 31;
-  const int blk = xcd_remap(blockIdx.x, gridDim.x);  // (b*H + h)*nqb + i
+  int blk = xcd_remap(blockIdx.x, gridDim.x);  // (b*H + h)*nqb + i
+  if (order) {  // the caller's processing order; rows outside the grid are skipped
+    blk = order[blk];
+    if (blk < 0 || blk >= int(gridDim.x)) return;
+  }
   const int i = blk % P.nqb, bh = blk / P.nqb;
   const int N = P.N;
   const int row0 = i * BQ;
@@ -336,13 +340,17 @@ __global__ __launch_bounds__(128) void attn_fwd_f32(Dims P, const float* __restr
                                                     const float* __restrict__ v, const int32_t* __restrict__ idx,
                                                     const float* __restrict__ weights,
                                                     const int32_t* __restrict__ counts, float* __restrict__ out,
-                                                    float* __restrict__ lse) {
+                                                    float* __restrict__ lse, const int32_t* __restrict__ order) {
   constexpr int TS = 32;
   __shared__ float Kt[TS][D];
   __shared__ float Vv[TS][D];
   __shared__ int skey[TS];
   __shared__ float slw[TS];
-  const int blk = blockIdx.x;
+  int blk = blockIdx.x;
+  if (order) {  // the caller's processing order; rows outside the grid are skipped
+    blk = order[blk];
+    if (blk < 0 || blk >= int(gridDim.x)) return;
+  }
   const int i = blk % P.nqb, bh = blk / P.nqb;
   const int N = P.N, Bk = P.Bk, Bq = P.Bq;
   const int row0 = i * Bq;
@@ -410,33 +418,36 @@ __global__ __launch_bounds__(128) void attn_fwd_f32(Dims P, const float* __restr
 
 template <int D, int BQ, int BK>
 hipError_t launch_bf16(const Dims& P, const void* q, const void* k, const void* v, const int32_t* idx,
-                       const float* weights, const int32_t* counts, void* out, float* lse, hipStream_t s) {
+                       const float* weights, const int32_t* counts, void* out, float* lse, const int32_t* order,
+                       hipStream_t s) {
   hipLaunchKernelGGL((attn_fwd_bf16<D, BQ, BK>), dim3(P.B * P.H * P.nqb), dim3(AttnCfg<D, BQ, BK>::kThreads), 0, s,
                      P, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                     static_cast<const uint16_t*>(v), idx, weights, counts, static_cast<uint16_t*>(out), lse);
+                     static_cast<const uint16_t*>(v), idx, weights, counts, static_cast<uint16_t*>(out), lse, order);
   return hipGetLastError();
 }
 
 template <int D, int BQ>
 hipError_t launch_bf16_bk(const Dims& P, const void* q, const void* k, const void* v, const int32_t* idx,
-                          const float* weights, const int32_t* counts, void* out, float* lse, hipStream_t s) {
+                          const float* weights, const int32_t* counts, void* out, float* lse, const int32_t* order,
+                          hipStream_t s) {
   switch (P.Bk) {
-    case 16: return launch_bf16<D, BQ, 16>(P, q, k, v, idx, weights, counts, out, lse, s);
-    case 32: return launch_bf16<D, BQ, 32>(P, q, k, v, idx, weights, counts, out, lse, s);
-    case 64: return launch_bf16<D, BQ, 64>(P, q, k, v, idx, weights, counts, out, lse, s);
-    default: return launch_bf16<D, BQ, 128>(P, q, k, v, idx, weights, counts, out, lse, s);
+    case 16: return launch_bf16<D, BQ, 16>(P, q, k, v, idx, weights, counts, out, lse, order, s);
+    case 32: return launch_bf16<D, BQ, 32>(P, q, k, v, idx, weights, counts, out, lse, order, s);
+    case 64: return launch_bf16<D, BQ, 64>(P, q, k, v, idx, weights, counts, out, lse, order, s);
+    default: return launch_bf16<D, BQ, 128>(P, q, k, v, idx, weights, counts, out, lse, order, s);
   }
 }
 
 }  // namespace
 
 hipError_t launch_attn_fwd(const Dims& P, const void* q, const void* k, const void* v, const int32_t* idx,
-                           const float* weights, const int32_t* counts, void* out, float* lse, hipStream_t s) {
+                           const float* weights, const int32_t* counts, void* out, float* lse, const int32_t* order,
+                           hipStream_t s) {
   if (P.bf16) {
-    if (P.d == 128 && P.Bq == 128) return launch_bf16_bk<128, 128>(P, q, k, v, idx, weights, counts, out, lse, s);
-    if (P.d == 128) return launch_bf16_bk<128, 64>(P, q, k, v, idx, weights, counts, out, lse, s);
-    if (P.Bq == 128) return launch_bf16_bk<64, 128>(P, q, k, v, idx, weights, counts, out, lse, s);
-    return launch_bf16_bk<64, 64>(P, q, k, v, idx, weights, counts, out, lse, s);
+    if (P.d == 128 && P.Bq == 128) return launch_bf16_bk<128, 128>(P, q, k, v, idx, weights, counts, out, lse, order, s);
+    if (P.d == 128) return launch_bf16_bk<128, 64>(P, q, k, v, idx, weights, counts, out, lse, order, s);
+    if (P.Bq == 128) return launch_bf16_bk<64, 128>(P, q, k, v, idx, weights, counts, out, lse, order, s);
+    return launch_bf16_bk<64, 64>(P, q, k, v, idx, weights, counts, out, lse, order, s);
   }
   const dim3 grid(P.B * P.H * P.nqb);
   auto Q = static_cast<const float*>(q);
@@ -444,9 +455,9 @@ hipError_t launch_attn_fwd(const Dims& P, const void* q, const void* k, const vo
   auto Vp = static_cast<const float*>(v);
   auto O = static_cast<float*>(out);
   if (P.d == 128)
-    hipLaunchKernelGGL(attn_fwd_f32<128>, grid, dim3(P.Bq), 0, s, P, Q, Kp, Vp, idx, weights, counts, O, lse);
+    hipLaunchKernelGGL(attn_fwd_f32<128>, grid, dim3(P.Bq), 0, s, P, Q, Kp, Vp, idx, weights, counts, O, lse, order);
   else
-    hipLaunchKernelGGL(attn_fwd_f32<64>, grid, dim3(P.Bq), 0, s, P, Q, Kp, Vp, idx, weights, counts, O, lse);
+    hipLaunchKernelGGL(attn_fwd_f32<64>, grid, dim3(P.Bq), 0, s, P, Q, Kp, Vp, idx, weights, counts, O, lse, order);
   return hipGetLastError();
 }
 

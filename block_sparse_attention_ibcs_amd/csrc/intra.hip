@@ -58,13 +58,45 @@ __global__ __launch_bounds__(256) void intra_lists_kernel(Dims P, int layer, int
   if (threadIdx.x == 0) counts[row] = count;
 }
 
+// Processing order for the attention kernel: Scatter rows sharing an offset (hence
+// one list) are placed next to each other, so the workgroups an XCD holds at once
+// read the same keys; Gather keeps the natural order (its neighbourhoods are already
+// contiguous). Position k of head bh's run: with U = L / q_block offsets and
+// NQB = a U + r, offsets u < r have a + 1 query blocks and the rest a; the position
+// runs over offsets, and within an offset over neighbourhoods.
+__global__ __launch_bounds__(256) void intra_order_kernel(Dims P, int layer, int L, int32_t* __restrict__ order) {
+  const int pos = blockIdx.x * blockDim.x + threadIdx.x;
+  const int rows = P.B * P.H * P.nqb;
+  if (pos >= rows) return;
+  const int bh = pos / P.nqb, k = pos % P.nqb;
+  int i = k;
+  if (layer == AB_INTRA_SCATTER) {
+    const int U = L / P.Bq;
+    const int a = P.nqb / U, r = P.nqb % U;
+    int u, p;
+    if (k < r * (a + 1)) {
+      u = k / (a + 1);
+      p = k % (a + 1);
+    } else {
+      const int k2 = k - r * (a + 1);  // a > 0 here: positions past the first r runs exist only then
+      u = r + k2 / a;
+      p = k2 % a;
+    }
+    i = p * U + u;
+  }
+  order[pos] = bh * P.nqb + i;
+}
+
 }  // namespace
 
 hipError_t launch_intra_lists(const Dims& P, int layer, int partition_tokens, int32_t* idx, float* weights,
-                              int32_t* counts, hipStream_t s) {
+                              int32_t* counts, int32_t* row_order, hipStream_t s) {
   const int rows = P.B * P.H * P.nqb;
   hipLaunchKernelGGL(intra_lists_kernel, dim3(rows), dim3(256), 0, s, P, layer, partition_tokens, idx, weights,
                      counts);
+  if (row_order)
+    hipLaunchKernelGGL(intra_order_kernel, dim3(ceil_div(rows, 256)), dim3(256), 0, s, P, layer, partition_tokens,
+                       row_order);
   return hipGetLastError();
 }
 

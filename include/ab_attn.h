@@ -203,13 +203,34 @@ int32_t ab_sample_topk(const ab_desc* desc, const float* scores, double density,
  *           first counts[b,h,i] entries of each row written (the rest untouched).
  * weights:  device fp32 [B, H, NQB, NKB]: 1.0 for the written entries.
  * counts:   device int32 [B, H, NQB].
+ * row_order: NULL, or device int32 [B * H * NQB] receiving a processing order for
+ *           ab_attn_fwd_ordered: Scatter rows ((b*H + h)*NQB + i) grouped by their
+ *           offset (rows of one offset share one list, so the workgroups resident
+ *           together read the same keys); Gather rows in their natural order.
  * Errors: AB_ERR_PARAM for another layer value or an L that is not a multiple of
- * q_block in [q_block, 2^30]; AB_ERR_NULL for NULL outputs.
+ * q_block in [q_block, 2^30]; AB_ERR_NULL for NULL lists.
  */
 #define AB_INTRA_SCATTER 0
 #define AB_INTRA_GATHER 1
 int32_t ab_intra_lists(const ab_desc* desc, int32_t layer, int32_t partition_tokens, int32_t* idx,
-                       float* weights, int32_t* counts, void* stream);
+                       float* weights, int32_t* counts, int32_t* row_order, void* stream);
+
+/*
+ * ab_attn_fwd with the query-block rows taken in a given order: the same outputs
+ * for every order (each row's computation is unchanged); only which rows run side
+ * by side, and so share caches, changes. For callers whose lists repeat across
+ * rows that are not neighbours (for instance INTRA Scatter, see ab_intra_lists).
+ *
+ * row_order: device int32 [B * H * NQB]: entry w is the row ((b*H + h)*NQB + i)
+ *            that the w-th workgroup computes (after the XCD-aware remapping of
+ *            workgroup ids). A permutation gives exactly ab_attn_fwd's result;
+ *            entries outside [0, B*H*NQB) are skipped, a row not listed is not
+ *            written and a row listed twice is written twice with the same values.
+ * Other arguments and errors as ab_attn_fwd; AB_ERR_NULL when row_order is NULL.
+ */
+int32_t ab_attn_fwd_ordered(const ab_desc* desc, const void* q, const void* k, const void* v,
+                            const int32_t* idx, const float* weights, const int32_t* counts,
+                            const int32_t* row_order, void* out, float* lse, void* stream);
 
 /*
  * Weighted block-sparse attention forward (AB-Attention abstract, problem,

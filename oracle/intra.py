@@ -80,3 +80,14 @@ def token_mask(n_tokens, q_block, k_block, lists):
         for j in idx[i, :cnt[i]]:
             M[rows, j * k_block:min(N, (j + 1) * k_block)] = True
     return M
+
+
+def intra_row_order(n_tokens, q_block, partition, layer):
+    """Processing order of one head's query blocks for the attention: Scatter blocks
+    grouped by their offset (blocks of one offset share one list), within an offset
+    by neighbourhood; Gather blocks in their natural order."""
+    nqb = -(-int(n_tokens) // int(q_block))
+    if layer == "gather":
+        return np.arange(nqb, dtype=np.int32)
+    U = int(partition) // int(q_block)
+    return np.array([p * U + u for u in range(U) for p in range(-(-nqb // U)) if p * U + u < nqb], dtype=np.int32)

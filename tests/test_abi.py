@@ -207,11 +207,26 @@ def test_intra_lists_validation():
     lib = _lib()
     cd = _desc().c()
     fake = ctypes.c_void_p(256)
-    assert lib.ab_intra_lists(ctypes.byref(cd), 2, 0, fake, fake, fake, None) == -3
-    assert lib.ab_intra_lists(ctypes.byref(cd), -1, 0, fake, fake, fake, None) == -3
+    assert lib.ab_intra_lists(ctypes.byref(cd), 2, 0, fake, fake, fake, None, None) == -3
+    assert lib.ab_intra_lists(ctypes.byref(cd), -1, 0, fake, fake, fake, None, None) == -3
     for L in (64, 192, -128, (1 << 30) + 128):  # below q_block, not a multiple of it, negative, too large
-        assert lib.ab_intra_lists(ctypes.byref(cd), 0, L, fake, fake, fake, None) == -3, L
+        assert lib.ab_intra_lists(ctypes.byref(cd), 0, L, fake, fake, fake, fake, None) == -3, L
     assert b"partition_tokens" in lib.ab_last_error()
-    assert lib.ab_intra_lists(ctypes.byref(cd), 1, 2048, None, fake, fake, None) == -1
-    assert lib.ab_intra_lists(ctypes.byref(cd), 1, 0, fake, fake, None, None) == -1
-    assert lib.ab_intra_lists(ctypes.byref(_desc(q_block=32).c()), 0, 0, fake, fake, fake, None) == -3
+    assert lib.ab_intra_lists(ctypes.byref(cd), 1, 2048, None, fake, fake, None, None) == -1
+    assert lib.ab_intra_lists(ctypes.byref(cd), 1, 0, fake, fake, None, fake, None) == -1
+    assert lib.ab_intra_lists(ctypes.byref(_desc(q_block=32).c()), 0, 0, fake, fake, fake, None, None) == -3
+
+
+def test_attn_fwd_ordered_validation():
+    lib = _lib()
+    cd = _desc().c()
+    fake = ctypes.c_void_p(256)
+    args = [fake] * 8  # q k v idx weights counts row_order out
+    for i in range(8):
+        a = list(args)
+        a[i] = None
+        assert lib.ab_attn_fwd_ordered(ctypes.byref(cd), *a, None, None) == -1, i
+    a = list(args)
+    a[0] = ctypes.c_void_p(256 + 8)
+    assert lib.ab_attn_fwd_ordered(ctypes.byref(cd), *a, None, None) == -2
+    assert lib.ab_attn_fwd_ordered(ctypes.byref(_desc(d=96).c()), *args, None, None) == -2

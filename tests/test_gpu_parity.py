@@ -26,7 +26,7 @@ import block_sparse_attention_ibcs_amd as ab
 import workloads
 from oracle import (Params, dense_attention, kmeans_fp32, block_scores, sample_rows, sample_rows_systematic,
                     sparse_ht_attention, topk_rows)
-from oracle.intra import default_partition, intra_lists
+from oracle.intra import default_partition, intra_lists, intra_row_order
 from oracle.sip import SIP_ONE
 
 pytestmark = pytest.mark.gpu
@@ -674,17 +674,24 @@ class _IntraRun:
         qd, kd, vd = (_to_dev(x, tdt) for x in (self.q, self.k, self.v))
         self.desc = ab.Desc.for_tensor(qd, w.q_block, w.k_block, w.n_clusters, w.kmeans_iters)
         self.scale = 1.0 / math.sqrt(w.d)
-        idx, wts, cnt = ab.ab_intra_lists(self.desc, layer, partition, device=qd.device)
+        idx, wts, cnt, order = ab.ab_intra_lists(self.desc, layer, partition, want_order=True, device=qd.device)
         out, lse = ab.ab_attn_fwd(self.desc, qd, kd, vd, idx, wts, cnt)
+        out2, lse2 = ab.ab_attn_fwd_ordered(self.desc, qd, kd, vd, idx, wts, cnt, order)
         torch.cuda.synchronize()
         self.idx, self.wts, self.cnt = idx.cpu().numpy(), wts.cpu().numpy(), cnt.cpu().numpy()
+        self.order = order.cpu().numpy()
         self.out, self.lse = out.float().cpu().numpy(), lse.cpu().numpy()
+        # the processing order changes nothing in the results
+        assert torch.equal(out2, out) and torch.equal(lse2, lse)
 
 
 def _check_intra_lists(run, layer, partition):
     w = run.w
     L = partition or default_partition(w.N, w.q_block)
-    ref_idx, ref_w, ref_cnt = intra_lists(w.N, w.q_block, w.k_block, L, "gather" if layer == ab.AB_INTRA_GATHER else "scatter")
+    name = "gather" if layer == ab.AB_INTRA_GATHER else "scatter"
+    ref_idx, ref_w, ref_cnt = intra_lists(w.N, w.q_block, w.k_block, L, name)
+    head_order = intra_row_order(w.N, w.q_block, L, name)
+    assert np.array_equal(run.order, np.concatenate([bh * w.nqb + head_order for bh in range(w.B * w.H)]))
     for b in range(w.B):
         for h in range(w.H):
             assert np.array_equal(run.cnt[b, h], ref_cnt), (b, h)
@@ -730,3 +737,35 @@ def test_intra_video_shape(layer):
     run = _IntraRun(w, workloads.generate(w, seed=0), layer, 0)
     _check_intra_lists(run, layer, 0)
     check_attention(run, Run.blocks(run, max_blocks=12))
+
+
+def test_attn_ordered_any_permutation_and_skips():
+    """ab_attn_fwd_ordered: a random row permutation gives ab_attn_fwd's outputs bit for
+    bit on SIP lists; rows whose order entry is out of range are not written."""
+    run = _run("wan1.3b")
+    d = run.desc
+    rows = d.B * d.H * d.nqb
+    perm = torch.from_numpy(np.random.default_rng(3).permutation(rows).astype(np.int32)).cuda()
+    out, lse = ab.ab_attn_fwd_ordered(d, run.qd, run.kd, run.vd, run.idx_d, run.wts_d, run.cnt_d, perm)
+    torch.cuda.synchronize()
+    assert torch.equal(out, run.out_d) and torch.equal(lse, run.lse_d)
+    # entries -1 and rows (out of range) skip their workgroup: those rows keep the sentinel
+    skip = perm.clone()
+    skip[::7] = -1
+    skip[3::11] = rows
+    missing = sorted(set(range(rows)) - set(skip.cpu().numpy().tolist()))
+    out2 = torch.full_like(out, 7.0)
+    lse2 = torch.full_like(lse, 7.0)
+    ab.ab_attn_fwd_ordered(d, run.qd, run.kd, run.vd, run.idx_d, run.wts_d, run.cnt_d, skip, out=out2, lse=lse2)
+    torch.cuda.synchronize()
+    o2 = out2.view(d.B * d.H, d.N, d.d)
+    ref = run.out_d.view(d.B * d.H, d.N, d.d)
+    for r in missing[:50]:
+        bh, i = divmod(r, d.nqb)
+        sl = slice(i * d.q_block, min(d.N, (i + 1) * d.q_block))
+        assert torch.all(o2[bh, sl] == 7.0)
+    written = [r for r in range(rows) if r not in set(missing)][:50]
+    for r in written:
+        bh, i = divmod(r, d.nqb)
+        sl = slice(i * d.q_block, min(d.N, (i + 1) * d.q_block))
+        assert torch.equal(o2[bh, sl], ref[bh, sl])

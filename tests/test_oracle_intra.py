@@ -15,7 +15,7 @@
 import numpy as np
 import pytest
 
-from oracle.intra import default_partition, intra_lists, token_mask
+from oracle.intra import default_partition, intra_lists, intra_row_order, token_mask
 
 SHAPES = [
     # (N, Bq, Bk, L)
@@ -112,3 +112,20 @@ def test_rejects_bad_partitions():
         intra_lists(512, 64, 16, 0, "gather")
     with pytest.raises(ValueError):
         intra_lists(512, 64, 16, 128, "relay")
+
+
+@pytest.mark.parametrize("N,Bq,Bk,L", SHAPES + [(32760, 128, 32, 2048), (5000, 128, 16, 4096)])
+def test_scatter_row_order_groups_shared_lists(N, Bq, Bk, L):
+    """The Scatter processing order lists every query block once, and the blocks that
+    share a list (equal offsets) form consecutive runs in ascending neighbourhood order."""
+    order = intra_row_order(N, Bq, L, "scatter")
+    nqb = -(-N // Bq)
+    assert sorted(order.tolist()) == list(range(nqb))
+    idx, _, cnt = intra_lists(N, Bq, Bk, L, "scatter")
+    offs = (order * Bq) % L
+    assert np.all(np.diff(offs) >= 0)  # runs of equal offset, offsets ascending
+    for a, b in zip(order[:-1], order[1:]):
+        if (a * Bq) % L == (b * Bq) % L:  # same run: next neighbourhood, same list
+            assert b > a
+            assert np.array_equal(idx[a, :cnt[a]], idx[b, :cnt[b]])
+    assert np.array_equal(intra_row_order(N, Bq, L, "gather"), np.arange(nqb))
