@@ -730,11 +730,19 @@ def test_intra_patterns(N, H, d, Bq, Bk, L, layer):
 
 
 @pytest.mark.parametrize("layer", [0, 1])
-def test_intra_video_shape(layer):
-    """The Wan2.1-1.3B shape (32760 tokens, 12 heads) with the default neighbourhood
-    (2048 tokens, a partial last one): lists on every row, attention on sampled blocks."""
-    w = workloads.get("wan1.3b")
-    run = _IntraRun(w, workloads.generate(w, seed=0), layer, 0)
+@pytest.mark.parametrize("name", ["wan1.3b", "hunyuan"])
+def test_intra_video_shape(name, layer):
+    """Video shapes with the default neighbourhood (a partial last one in both): the
+    Wan2.1-1.3B shape (32760 tokens, all 12 heads, 2048-token neighbourhoods) and the
+    HunyuanVideo shape (118800 tokens, k_block 16, 3968-token neighbourhoods; its first
+    and last head): lists on every row, attention on sampled blocks."""
+    w = workloads.get(name)
+    q, k, v = workloads.generate(w, seed=0)
+    if name == "hunyuan":
+        sel = [0, w.H - 1]
+        q, k, v = (np.ascontiguousarray(x[:, sel]) for x in (q, k, v))
+        w = w.with_(H=2)
+    run = _IntraRun(w, (q, k, v), layer, 0)
     _check_intra_lists(run, layer, 0)
     check_attention(run, Run.blocks(run, max_blocks=12))
 
