@@ -603,7 +603,7 @@ def test_injected_index_lists_bf16():
         assert np.abs(lse[0, 0, lo:hi] - l_ref).max() <= 1e-3 * max(1.0, np.abs(l_ref).max())
 
 
-def _seed_means(desc, qd, kd, vd, density, seeds, unit_weights=False):
+def _seed_means(desc, qd, kd, vd, density, seeds, unit_weights=False, sampler="sip"):
     """Per-row means and standard errors over sampling seeds of the weighted estimate's
     denominator exp(LSE) and numerator O exp(LSE), both relative to the dense
     denominator, from the GPU sampler and attention kernel (scores computed once).
@@ -613,7 +613,8 @@ def _seed_means(desc, qd, kd, vd, density, seeds, unit_weights=False):
     scores = ab.ab_score(desc, qd, kd)
     acc = {n: 0.0 for n in ("num", "num2", "den", "den2")}
     for seed in range(seeds):
-        idx, wts, cnt, _ = ab.ab_sample(desc, scores, density, seed, want_mask=False)
+        draw = ab.ab_sample if sampler == "sip" else ab.ab_sample_systematic
+        idx, wts, cnt, _ = draw(desc, scores, density, seed, want_mask=False)
         if unit_weights:
             wts = torch.ones_like(wts)
         out, lse = ab.ab_attn_fwd(desc, qd, kd, vd, idx, wts, cnt)
@@ -628,12 +629,14 @@ def _seed_means(desc, qd, kd, vd, density, seeds, unit_weights=False):
     return mean, se, o_dense
 
 
+@pytest.mark.parametrize("sampler", ["sip", "systematic"])
 @pytest.mark.parametrize("case", ["tiny-fp32", "bf16-d128"])
-def test_gpu_estimate_is_unbiased(case):
+def test_gpu_estimate_is_unbiased(case, sampler):
     """SIP sentence: sampling in proportion to the scores and reweighting by the inverse
     inclusion probability makes one pass an unbiased estimate of dense attention. The
     GPU path's numerator and denominator, averaged over sampling seeds, lie within five
-    standard errors of exact dense attention (float64 on the CPU)."""
+    standard errors of exact dense attention (float64 on the CPU); also for the
+    systematic draw, which has the same inclusion probabilities."""
     dev = _gpu()
     if case == "tiny-fp32":
         w = workloads.get("tiny")
@@ -651,7 +654,7 @@ def test_gpu_estimate_is_unbiased(case):
         # the kernel's bf16 probabilities and output add a deterministic error of up to
         # about 2^-8 relative on top of the sampling noise
         density, seeds, tol = 0.2, 300, 2.0 ** -8
-    mean, se, o_dense = _seed_means(desc, qd, kd, vd, density, seeds)
+    mean, se, o_dense = _seed_means(desc, qd, kd, vd, density, seeds, sampler=sampler)
     assert np.all(np.abs(mean["den"] - 1.0) <= 5 * se["den"] + tol)
     scale = np.abs(o_dense).max()
     assert np.all(np.abs(mean["num"] - o_dense) <= 5 * se["num"] + tol * scale)
@@ -659,7 +662,7 @@ def test_gpu_estimate_is_unbiased(case):
     assert se["den"].max() > 0
     # and the check has power: without the inverse-probability weights the same draws
     # underestimate the denominator far beyond five standard errors
-    mean1, se1, _ = _seed_means(desc, qd, kd, vd, density, seeds // 4, unit_weights=True)
+    mean1, se1, _ = _seed_means(desc, qd, kd, vd, density, seeds // 4, unit_weights=True, sampler=sampler)
     assert np.mean(np.abs(mean1["den"] - 1.0) > 5 * se1["den"] + tol) > 0.5
 
 
