@@ -23,9 +23,10 @@
 // every 16-lane row), so the loop reads no LDS; the two halves then merge their
 // minima (lower index wins ties). The update uses per-cluster member lists built
 // with wave ballots; a wave owns whole clusters and sums their members for its
-// lane's dims in ascending row order from the block's copy in LDS, and the norm
-// tree is a butterfly of xor shuffles (the adds commute exactly, so every lane
-// ends with the tree's value).
+// lane's dims in ascending row order from the block's copy in LDS (bf16 rows of
+// 128 dims: one 32-bit read of a dim pair per member), and the norm tree is a
+// butterfly of xor shuffles (the adds commute exactly, so the lane holding the
+// tree's root ends with its value).
 #include "ab_internal.h"
 
 namespace ab {
@@ -322,6 +323,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BF16 ? 4 : 
 #pragma unroll
       for (int g = 0; g < G; ++g) npart[c * G + g] = t[g];
   };
+  // bf16 rows of 128 dims in the update: lane l holds dims 2l and 2l+1 (one 32-bit
+  // read per member). Its halving tree: dims k and k+32 are lanes l and l^16, k and
+  // k+16 lanes l and l^8, ..., k and k+2 lanes l and l^1, then k and k+1 the two
+  // halves of lane 0 (dims 0-63) and of lane 32 (dims 64-127).
+  constexpr bool kPairs = BF16 && D == 128;
+  auto finish_pair = [&](int c, float mu0, float mu1) {
+    m2_t[(2 * lane) * CP + c] = -2.0f * mu0;  // exact
+    m2_t[(2 * lane + 1) * CP + c] = -2.0f * mu1;
+    float t0 = mul_rn(mu0, mu0), t1 = mul_rn(mu1, mu1);
+#pragma unroll
+    for (int sh = 16; sh >= 1; sh >>= 1) {
+      t0 = add_rn(t0, __shfl_xor(t0, sh, 64));
+      t1 = add_rn(t1, __shfl_xor(t1, sh, 64));
+    }
+    const float t = add_rn(t0, t1);
+    if ((lane & 31) == 0) npart[c * G + (lane >> 5)] = t;
+  };
   for (int c = wave; c < Ci; c += nthr >> 6) {
     float mu[G];
 #pragma unroll
@@ -413,6 +431,41 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BF16 ? 4 : 
     // row order, the G chains side by side. Member rows are fetched eight at a time
     // ahead of the in-order adds, and the next eight list entries while those rows
     // are read.
+    if constexpr (kPairs) {
+      const uint32_t* Xw = reinterpret_cast<const uint32_t*>(X);  // [Bq][64] bf16 pairs
+      for (int c = wave; c < Ci; c += nthr >> 6) {
+        const int cnt = ccount[c];
+        float mu0, mu1;
+        if (cnt > 0) {
+          const uint8_t* lc = list + c * Bq;
+          float s0 = 0.0f, s1 = 0.0f;
+          int m = 0;
+          uint2 rr = *reinterpret_cast<const uint2*>(lc);
+          for (; m + 8 <= cnt; m += 8) {
+            uint32_t v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = Xw[int(((u < 4 ? rr.x : rr.y) >> (8 * (u & 3))) & 0xFFu) * 64 + lane];
+            rr = *reinterpret_cast<const uint2*>(lc + min(m + 8, Bq - 8));
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+              s0 = add_rn(s0, __uint_as_float(v[u] << 16));
+              s1 = add_rn(s1, __uint_as_float(v[u] & 0xFFFF0000u));
+            }
+          }
+          for (; m < cnt; ++m) {
+            const uint32_t w = Xw[int(lc[m]) * 64 + lane];
+            s0 = add_rn(s0, __uint_as_float(w << 16));
+            s1 = add_rn(s1, __uint_as_float(w & 0xFFFF0000u));
+          }
+          mu0 = __fdiv_rn(s0, float(cnt));
+          mu1 = __fdiv_rn(s1, float(cnt));
+        } else {
+          mu0 = -0.5f * m2_t[(2 * lane) * CP + c];  // kept centroid
+          mu1 = -0.5f * m2_t[(2 * lane + 1) * CP + c];
+        }
+        finish_pair(c, mu0, mu1);
+      }
+    } else
     for (int c = wave; c < Ci; c += nthr >> 6) {
       const int cnt = ccount[c];
       float mu[G];
