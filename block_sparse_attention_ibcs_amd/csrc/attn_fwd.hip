@@ -230,14 +230,41 @@ void attn_fwd_bf16(Dims P, const uint16_t* __restrict__ q, const uint16_t* __res
     f32x16_t acc[2];
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) acc[hb] = f32x16_t{};
+    // The K fragments of step kk + 1 are read before the products of step kk are
+    // issued, so each read has two products' time to land (the scheduling-group
+    // barriers keep the compiler from sinking the reads next to their use).
+    {
+      uint4 kf[2][2];
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
+      for (int hb = 0; hb < 2; ++hb) kf[0][hb] = *reinterpret_cast<const uint4*>(kc + hb * 32 * Cfg::kRowBytes + koff[0]);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
 #pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-        const uint4 a = *reinterpret_cast<const uint4*>(kc + hb * 32 * Cfg::kRowBytes + koff[kk]);
-        acc[hb] = mfma32x32x16(as_bf16x8(a), qf[kk], acc[hb]);
+      for (int kk = 0; kk < D / 16; ++kk) {
+        if (kk + 1 < D / 16) {
+#pragma unroll
+          for (int hb = 0; hb < 2; ++hb)
+            kf[(kk + 1) & 1][hb] = *reinterpret_cast<const uint4*>(kc + hb * 32 * Cfg::kRowBytes + koff[kk + 1]);
+          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+        }
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) acc[hb] = mfma32x32x16(as_bf16x8(kf[kk & 1][hb]), qf[kk], acc[hb]);
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
       }
     }
+    // The V operands of the first D/32 products of O^T += V^T P^T are read now, so
+    // they land while the softmax runs; the rest follow one 32-dim block behind the
+    // products (a ring of D/32 operands).
+    constexpr int kVdb = D / 32;
+    uint4 vf[kVdb];
+    auto vread = [&](int i) {  // operand of product i: 16-slot group i / kVdb, dim block i % kVdb
+      const unsigned char* vrow = vc + 16 * (i / kVdb) * Cfg::kRowBytes;
+      const uint2 lo = lds_read_tr16(vrow + voff[i % kVdb]);
+      const uint2 hi = lds_read_tr16(vrow + 8 * Cfg::kRowBytes + voff[i % kVdb]);
+      vf[i % kVdb] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    };
+#pragma unroll
+    for (int i = 0; i < kVdb; ++i) vread(i);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kVdb, 0);
     // padding slots of the last tile get probability 0
     const bool ragged = (t + 1) * kSlots > vend;
     if (ragged) {
@@ -298,15 +325,14 @@ void attn_fwd_bf16(Dims P, const uint16_t* __restrict__ q, const uint16_t* __res
       probs();
     }
     l += ps;
-    // O^T += V^T P^T over four 16-slot groups; four independent accumulators
+    // O^T += V^T P^T over four 16-slot groups; D/32 independent accumulators
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const unsigned char* vrow = vc + 16 * g * Cfg::kRowBytes;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const uint2 lo = lds_read_tr16(vrow + voff[db]);
-        const uint2 hi = lds_read_tr16(vrow + 8 * Cfg::kRowBytes + voff[db]);
-        o[db] = mfma32x32x16(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), pb[g], o[db]);
+    for (int i = 0; i < 4 * kVdb; ++i) {
+      o[i % kVdb] = mfma32x32x16(as_bf16x8(vf[i % kVdb]), pb[i / kVdb], o[i % kVdb]);
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 1);
+      if (i + kVdb < 4 * kVdb) {
+        vread(i + kVdb);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 1);
       }
     }
   };
