@@ -325,7 +325,11 @@ void attn_fwd_bf16(Dims P, const uint16_t* __restrict__ q, const uint16_t* __res
       probs();
     }
     l += ps;
-    // O^T += V^T P^T over four 16-slot groups; D/32 independent accumulators
+    // O^T += V^T P^T over four 16-slot groups; D/32 independent accumulators. The
+    // wave raises its issue priority for these products, so on a SIMD shared with a
+    // wave that is in its softmax the matrix core is fed first and the other wave's
+    // VALU work fills the gaps.
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int i = 0; i < 4 * kVdb; ++i) {
       o[i % kVdb] = mfma32x32x16(as_bf16x8(vf[i % kVdb]), pb[i / kVdb], o[i % kVdb]);
@@ -335,6 +339,7 @@ void attn_fwd_bf16(Dims P, const uint16_t* __restrict__ q, const uint16_t* __res
         __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 1);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
   };
   for (int t = 0; t < ntiles; t += 2) {
     step(t, k0s, v0s, k1s, v1s);
