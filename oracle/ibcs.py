@@ -25,8 +25,11 @@ algorithm nor the estimate's formula. Readings used here:
   ascending row order, divided by the member count with one correctly rounded
   fp32 division.
 * Each cluster stands in for its members by its centroid. For bf16 inputs the
-  centroid is rounded to bf16 (ties to even) before it meets the keys, since
-  that is the precision the keys have.
+  centroid meets the keys at the keys' precision: it is multiplied in fp32 by
+  c2 = fl32(fl32(scale) * fl32(log2 e)) and the product is rounded to bf16 (ties
+  to even), so the logit in base-2 units is the exact dot product of that bf16
+  vector with the key (one rounding of the scaled centroid, as one rounding of
+  the centroid itself would be; the pages fix neither).
 * Estimate: s_ij = sum_c (n_c / n_i) * exp(l_cj - L_c) with
   l_cj = log sum_{k in j} exp(scale * mu_c . k_k) and L_c = log sum_j exp(l_cj),
   i.e. the mean softmax mass that block i's queries put on sub-block j when
@@ -173,12 +176,15 @@ def block_scores(mu, sizes, n_rows, K, k_block, scale, bf16):
     Returns float32 [NKB].
     """
     mu = np.asarray(mu, dtype=np.float32)
-    if bf16:
-        mu = round_bf16(mu)
     K = np.asarray(K, dtype=np.float64)
     N = K.shape[0]
     nkb = -(-N // k_block)
-    logits = float(scale) * (mu.astype(np.float64) @ K.T)  # [C, N]
+    if bf16:
+        c2 = np.float32(np.float32(scale) * np.float32(np.log2(np.e)))
+        mu2 = round_bf16((mu * c2).astype(np.float32))  # scale * log2(e) * mu at bf16
+        logits = np.log(2.0) * (mu2.astype(np.float64) @ K.T)  # base-2 logits in natural units
+    else:
+        logits = float(scale) * (mu.astype(np.float64) @ K.T)  # [C, N]
     pad = nkb * k_block - N
     if pad:
         logits = np.concatenate([logits, np.full((logits.shape[0], pad), -np.inf)], axis=1)

@@ -154,6 +154,31 @@ def test_kmeans_tie_goes_to_lowest_cluster_and_empty_cluster_kept():
     np.testing.assert_array_equal(mu2[1], X2[2])  # the empty cluster keeps its centroid
 
 
+def test_bf16_estimate_uses_the_scaled_centroid_at_bf16(tiny_inputs):
+    """For bf16 inputs the centroid meets the keys as bf16(fl32(c2 * mu)) with
+    c2 = fl32(scale * log2 e), the logits being base-2. Centroids chosen so that
+    c2 * mu rounds to a given bf16 vector t make that rounding the identity: the
+    estimate must then equal the unrounded fp32 estimate at mu = t / (scale log2 e)
+    (the two differ only by mu's own fp32 rounding). Rounding mu before scaling,
+    a missing ln 2 or a wrong constant moves the scores well past that comparison's tolerance."""
+    w, q, k, v = tiny_inputs
+    scale = 1.0 / math.sqrt(w.d)
+    rng = np.random.default_rng(11)
+    c2 = np.float32(np.float32(scale) * np.float32(1.4426950408889634))
+    t = round_bf16((rng.standard_normal((4, w.d)) * 4.0).astype(np.float32))
+    mu = (t.astype(np.float64) / float(c2)).astype(np.float32)
+    assert np.array_equal(round_bf16((mu * c2).astype(np.float32)), t)
+    sizes = np.array([30, 20, 10, 4], dtype=np.int32)
+    K = k[0, 0]
+    s_bf16 = block_scores(mu, sizes, 64, K, w.k_block, scale, bf16=True).astype(np.float64)
+    exact = (t.astype(np.float64) / (np.float64(np.float32(scale)) * np.log2(np.e))).astype(np.float32)
+    s_ref = block_scores(exact, sizes, 64, K, w.k_block, scale, bf16=False).astype(np.float64)
+    np.testing.assert_allclose(s_bf16, s_ref, rtol=1e-5, atol=1e-9)
+    # the reading that rounds mu itself fails the same comparison
+    s_other = block_scores(round_bf16(mu), sizes, 64, K, w.k_block, scale, bf16=False).astype(np.float64)
+    assert not np.allclose(s_other, s_ref, rtol=1e-5, atol=1e-9)
+
+
 def test_bf16_rounding_matches_torch():
     rng = np.random.default_rng(5)
     x = np.concatenate([rng.standard_normal(10000).astype(np.float32) * 10, np.array([0.0, -0.0, 1.0, 3.0039062, 1e-40], dtype=np.float32)])
