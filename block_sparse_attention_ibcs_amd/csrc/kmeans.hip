@@ -509,12 +509,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BF16 ? 4 : 
   }
 
   // ---- outputs ----
+  // The bf16 copy is the matrix-core operand of the block estimate: the centroid
+  // times c2 = scale * log2(e) (one fp32 product, then one rounding to bf16), so the
+  // product with a key is the logit in base-2 units.
   const size_t cbase = size_t(blk) * C;
+  const float c2 = P.scale * 1.4426950408889634f;
   for (int p = tid; p < C * D; p += nthr) {
     const int c = p / D, k = p % D;
     const float v = c < Ci ? -0.5f * m2_t[k * CP + c] : 0.0f;  // -0.5 * (-2 mu) is exact
     if (cent) cent[(cbase + c) * D + k] = v;
-    if (cent_bf16) cent_bf16[(cbase + c) * D + k] = f32_to_bf16(v);
+    if (cent_bf16) cent_bf16[(cbase + c) * D + k] = f32_to_bf16(v * c2);
   }
   if (sizes_out)
     for (int c = tid; c < C; c += nthr) sizes_out[cbase + c] = (c < Ci) ? ccount[c] : 0;

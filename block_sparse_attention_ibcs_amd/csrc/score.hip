@@ -6,7 +6,8 @@
 //   s_ij = sum_c (n_c / n_i) exp(l_cj - L_c).
 //
 // Stage 1 (score_lse): per (b, h) the centroids form an [NQB*C, d] matrix that
-// is multiplied by the keys on the matrix cores. The product is computed
+// is multiplied by the keys on the matrix cores (the bf16 centroids carry
+// scale * log2 e, so the products are base-2 logits). The product is computed
 // transposed (keys x centroids), so each lane owns one centroid and 16 keys of
 // a 32-key block: sub-block log-sum-exps are in-register reductions plus one
 // exchange with the other half of the wave. Exponentials use a per-centroid
@@ -44,17 +45,22 @@ struct LseState {
   float sub;   // same, over the keys of the open sub-block (k_block >= 64)
 };
 
-// One centroid row group's epilogue for one 32-key block: logits x (this lane's 16
-// keys of the block), running state st, first key of the block kb.
+// One centroid row group's epilogue for one 32-key block: base-2 logits x (this
+// lane's 16 keys of the block; the centroid operand already carries scale * log2 e),
+// running state st, first key of the block kb.
+//
+// The first block sets the reference: its maximum, or 0 when that maximum lies in
+// [-40, 40] (then 2^x itself neither overflows nor loses the block's largest terms).
+// While every row of the wave keeps reference 0 the exponentials take the logits
+// as they are, one instruction per key instead of two. A block whose sum would
+// pass 2^64 raises the reference of the rows concerned, as before.
 template <int BK>
-__device__ __forceinline__ void lse_block(const f32x16_t& acc, LseState& st, float c2, int kb, int key_end,
-                                          int half, bool row_ok, float* ell_row, int C, int nkb) {
+__device__ __forceinline__ void lse_block(const f32x16_t& acc, LseState& st, int kb, int key_end, int half,
+                                          bool row_ok, float* ell_row, int C, int nkb) {
   // This lane's 16 keys: e < 8 lie in the block's first 16 keys, e >= 8 in the last 16.
   float ev[16];
   float s0, s1;  // this lane's sums over its keys of the first and of the last 16
-  auto exps = [&]() {
-#pragma unroll
-    for (int e = 0; e < 16; ++e) ev[e] = fast_exp2(__builtin_fmaf(acc[e], c2, -st.mref));
+  auto sums = [&]() {
     s0 = ev[0];
 #pragma unroll
     for (int e = 1; e < 8; ++e) s0 += ev[e];
@@ -62,19 +68,37 @@ __device__ __forceinline__ void lse_block(const f32x16_t& acc, LseState& st, flo
 #pragma unroll
     for (int e = 9; e < 16; ++e) s1 += ev[e];
   };
-  exps();
+  auto exps_ref = [&]() {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) ev[e] = fast_exp2(acc[e] - st.mref);
+    sums();
+  };
+  if (__builtin_amdgcn_ballot_w64(st.mref != 0.0f) == 0) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) ev[e] = fast_exp2(acc[e]);  // reference 0 in every row
+    sums();
+  } else {
+    exps_ref();
+  }
   float s_pair = pair_sum(s0 + s1);
-  // rebase when the reference is unset (first block) or a sum would pass 2^64
-  if (__builtin_amdgcn_ballot_w64(!(s_pair < 1.8446744e19f)) != 0) {
+  // rebase the rows whose reference is unset (first block: x + inf) or whose sum
+  // would pass 2^64
+  const bool rebase = !(s_pair < 1.8446744e19f);
+  if (__builtin_amdgcn_ballot_w64(rebase) != 0) {
     float bm = acc[0];
 #pragma unroll
     for (int e = 1; e < 16; ++e) bm = fmaxf(bm, acc[e]);
-    const float nref = fmaxf(st.mref, pair_max(bm) * c2);
-    const float f = fast_exp2(st.mref - nref);  // 0 when the old reference was unset
+    bm = pair_max(bm);
+    float nref = st.mref;
+    if (rebase) {
+      nref = fmaxf(st.mref, bm);
+      if (st.mref == -__builtin_inff() && nref >= -40.0f && nref <= 40.0f) nref = 0.0f;
+    }
+    const float f = fast_exp2(st.mref - nref);  // 0 when the old reference was unset, 1 when kept
     st.tot *= f;
     st.sub *= f;
     st.mref = nref;
-    exps();
+    exps_ref();
     s_pair = pair_sum(s0 + s1);
   }
   st.tot += s_pair;
@@ -117,7 +141,6 @@ void score_lse_bf16(Dims P, int split_keys, int splits, int row_tiles, const uin
   const int key_begin = split * split_keys;
   const int key_end = min(N, key_begin + split_keys);
   const int ntiles = ceil_div(key_end - key_begin, kTileKeys);
-  const float c2 = P.scale * kLog2e;
 
   // B operands: this lane's two centroid rows (row groups), 8 dims per 16-wide k step
   int cr[2];
@@ -189,7 +212,7 @@ void score_lse_bf16(Dims P, int split_keys, int splits, int row_tiles, const uin
         }
       }
 #pragma unroll
-      for (int rg = 0; rg < 2; ++rg) lse_block<BK>(acc[rg], st[rg], c2, kb, key_end, half, row_ok[rg], ell_row[rg], P.C, P.nkb);
+      for (int rg = 0; rg < 2; ++rg) lse_block<BK>(acc[rg], st[rg], kb, key_end, half, row_ok[rg], ell_row[rg], P.C, P.nkb);
     }
   };
   for (int t = 0; t < ntiles; t += 2) {

@@ -104,8 +104,9 @@ size_t ab_score_workspace_size(const ab_desc* desc);
  * clusters keep their centroid with size 0), then
  *   scores[b,h,i,j] = sum_c (n_c/n_i) * exp(l_cj - L_c),
  *   l_cj = log sum_{k in sub-block j} exp(scale * mu_c . k_k),  L_c = log sum_j exp(l_cj),
- * with mu_c rounded to bf16 before the product for bf16 inputs. Each score row
- * sums to 1 (up to rounding).
+ * where for bf16 inputs the product is taken with bf16(fl32(c2 * mu_c)),
+ * c2 = fl32(scale * log2 e), as a base-2 logit (one rounding of the scaled
+ * centroid). Each score row sums to 1 (up to rounding).
  *
  * q, k:    device [B, H, N, d], dtype of desc.
  * scores:  device fp32 [B, H, NQB, NKB], written in full.
