@@ -24,8 +24,8 @@ import torch
 
 import block_sparse_attention_ibcs_amd as ab
 import workloads
-from oracle import (Params, dense_attention, kmeans_fp32, block_scores, sample_rows, sample_rows_systematic,
-                    sparse_ht_attention, topk_rows)
+from oracle import (Params, block_scores, dense_attention, kmeans_fp32, round_bf16, sample_rows,
+                    sample_rows_systematic, sparse_ht_attention, topk_rows)
 from oracle.intra import default_partition, intra_lists, intra_row_order
 from oracle.sip import SIP_ONE
 
@@ -407,6 +407,61 @@ def test_edge_shapes(N, H, d, Bq, Bk, C, T, density):
             err = np.abs(run.out[0, h] - o)
             assert np.all(err <= o_bound(o, TOL["bf16"]))
             assert np.linalg.norm(run.out[0, h] - o) / np.linalg.norm(o) <= 1e-2
+
+
+def _reference_path_inputs():
+    """Q, K, V (bf16 values, [1, 1, 1024, 128]) whose centroid logits reach every
+    branch of the scorer's running reference: query blocks 0, 2, 4, 5, 7 stay within
+    a few units of 0 (reference 0); block 1 has logits past +40 in base-2 units at
+    every 128-key boundary where a key split can start (reference = the first
+    block's maximum, and later blocks that outgrow it by more than 64); block 3 lies
+    below -40 everywhere; block 6 stays small until keys 960-991, whose logits pass
+    +64 in the middle of a split (a rebase of those rows only, the rest of the wave
+    keeping reference 0)."""
+    N, d = 1024, 128
+    rng = np.random.default_rng(3)
+    K = rng.standard_normal((N, d)).astype(np.float32)
+    c = np.full(d, 0.5, np.float32)
+    K += c
+    u = rng.standard_normal(d).astype(np.float32)
+    u *= math.sqrt(d) / np.linalg.norm(u)
+    K[960:992] = 0.3 * K[960:992] + 2.5 * u
+    Q = rng.standard_normal((N, d)).astype(np.float32)
+    u2 = rng.standard_normal(d).astype(np.float32)
+    u2 *= math.sqrt(d) / np.linalg.norm(u2)
+    Q[128:256] = 40.0 * (u2 + 0.3 * Q[128:256])
+    Q[384:512] = -30.0 * (c / 0.5 + 0.2 * Q[384:512])
+    Q[768:896] = 2.5 * u + 0.5 * Q[768:896]
+    V = rng.standard_normal((N, d)).astype(np.float32)
+    return [workloads.round_to_bf16(x[None, None]) for x in (Q, K, V)]
+
+
+def test_scorer_reference_paths():
+    """Scores, samples and attention on logits that need every reference case of the
+    scorer (and very large or very negative attention logits), against the oracle on
+    every block. The regimes are checked first with the oracle's own centroids."""
+    _gpu()
+    q, k, v = _reference_path_inputs()
+    w = workloads.Workload("refpaths", 1, 1, (1, 1, 1024), 128, "bf16", 128, 32, 8, 0.25, 0.5, False, kmeans_iters=4)
+    scale = 1.0 / math.sqrt(128)
+    c2 = np.float32(np.float32(scale) * np.float32(1.4426950408889634))
+    K = k[0, 0].astype(np.float64)
+    bmax = []
+    for i in range(8):
+        mu, sz, _ = kmeans_fp32(q[0, 0, i * 128:(i + 1) * 128], 8, 4)
+        lg = round_bf16((mu[sz > 0] * c2).astype(np.float32)).astype(np.float64) @ K.T
+        bmax.append(lg.reshape(lg.shape[0], 32, 32).max(axis=2))  # [rows, 32-key blocks]
+    for i in (0, 2, 4, 5, 7):
+        assert np.abs(bmax[i]).max() < 30
+    assert np.all(bmax[1].max(axis=0)[::4] > 40)
+    assert bmax[3].max() < -40
+    assert bmax[6][:, :30].max() < 30 and bmax[6][:, 30].max() > 70
+    run = Run(w, inputs=(q, k, v), seed=9)
+    blocks = run.blocks(64)
+    check_kmeans(run, blocks)
+    check_scores(run, blocks)
+    check_sampler(run, blocks)
+    check_attention(run, blocks)
 
 
 @pytest.mark.parametrize("nkb,density", [(37, 0.3), (1024, 0.1), (1000, 1.0), (1500, 0.02), (2363, 0.1),
