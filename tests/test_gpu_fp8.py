@@ -190,6 +190,16 @@ def test_attn_fp8_dense_and_peaked():
     _check_attn(q, k, v, 32, 1.0, seed=7)
 
 
+def test_attn_fp8_extreme_logits():
+    """Query blocks whose logits reach +-200 in base-2 units, lie below -40 everywhere,
+    or jump by more than 64 within a row's list (the inputs of the scorer's
+    reference-path test), every block against the exact FP8 computation."""
+    from test_gpu_parity import _reference_path_inputs
+
+    q, k, v = (torch.from_numpy(x).to(torch.bfloat16) for x in _reference_path_inputs())
+    _check_attn(q, k, v, 32, 0.5, seed=21)
+
+
 @pytest.mark.parametrize("name", ["wan1.3b", "hunyuan"])
 def test_attn_fp8_video_shape(name):
     """Full sequence length of the workload (its first and last head), sampled blocks
