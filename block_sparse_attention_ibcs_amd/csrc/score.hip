@@ -195,11 +195,22 @@ void score_lse_bf16(Dims P, int split_keys, int splits, int row_tiles, const uin
       const int kb = key_begin + t * kTileKeys + hb * 32;  // first key of this 32-key block (uniform)
       if (kb >= key_end) break;
       f32x16_t acc[2] = {f32x16_t{}, f32x16_t{}};
+      // the key fragment of step kk + 1 is read before the two products of step kk
+      // are issued (the scheduling-group barriers keep that order)
+      {
+        uint4 kf[2];
+        kf[0] = *reinterpret_cast<const uint4*>(kc + hb * 32 * Cfg::kRowBytes + koff[0]);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        const uint4 a = *reinterpret_cast<const uint4*>(kc + hb * 32 * Cfg::kRowBytes + koff[kk]);
-        acc[0] = mfma32x32x16(as_bf16x8(a), bfrag[0][kk], acc[0]);
-        acc[1] = mfma32x32x16(as_bf16x8(a), bfrag[1][kk], acc[1]);
+        for (int kk = 0; kk < D / 16; ++kk) {
+          if (kk + 1 < D / 16) {
+            kf[(kk + 1) & 1] = *reinterpret_cast<const uint4*>(kc + hb * 32 * Cfg::kRowBytes + koff[kk + 1]);
+            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+          }
+          acc[0] = mfma32x32x16(as_bf16x8(kf[kk & 1]), bfrag[0][kk], acc[0]);
+          acc[1] = mfma32x32x16(as_bf16x8(kf[kk & 1]), bfrag[1][kk], acc[1]);
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
+        }
       }
       if (kb + 32 > key_end) {  // ragged end of the keys
 #pragma unroll
