@@ -53,7 +53,8 @@ struct LseState {
 // [-40, 40] (then 2^x itself neither overflows nor loses the block's largest terms).
 // While every row of the wave keeps reference 0 the exponentials take the logits
 // as they are, one instruction per key instead of two. A block whose sum would
-// pass 2^64 raises the reference of the rows concerned, as before.
+// pass 2^64 raises the reference of those rows to the running maximum (the sums
+// so far are rescaled), and the block is redone against it.
 template <int BK>
 __device__ __forceinline__ void lse_block(const f32x16_t& acc, LseState& st, int kb, int key_end, int half,
                                           bool row_ok, float* ell_row, int C, int nkb) {
