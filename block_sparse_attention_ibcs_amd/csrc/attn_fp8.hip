@@ -297,7 +297,10 @@ void attn_fwd_fp8(Dims P, const uint8_t* __restrict__ qcode, const float* __rest
         word = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(a[e0 + e], a8, c8), e, word);
       pk[g] = int(word);
     }
-    // O^T += Vc^T P^T
+    // O^T += Vc^T P^T, the sums of P and the V-Smooth add-back: the wave raises its
+    // issue priority for these products (the other wave of the SIMD is then
+    // usually in its softmax, whose VALU work fills the gaps)
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
       i32x8_t a;
@@ -354,6 +357,7 @@ void attn_fwd_fp8(Dims P, const uint8_t* __restrict__ qcode, const float* __rest
       const uint32_t l23 = half == 0 ? ((u[2] >> 16) | (u[3] & 0xFFFF0000u)) : 0u;
       o[db] = mfma32x32x16(as_bf16x8(make_uint4(h01, h23, l01, l23)), bs, o[db]);
     }
+    __builtin_amdgcn_s_setprio(0);
   };
   for (int t = 0; t < ntiles; t += 2) {
     step(t, k0s, v0s, m0s, k1s, v1s, m1s);
