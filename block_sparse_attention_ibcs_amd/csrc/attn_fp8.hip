@@ -79,7 +79,7 @@ void attn_fwd_fp8(Dims P, const uint8_t* __restrict__ qcode, const float* __rest
   const int N = P.N;
   const int row0 = i * 128;
   const int n = min(128, N - row0);
-  const int cnt = counts[blk];
+  const int cnt = min(max(counts[blk], 0), P.nkb);  // clamped to the row: no read leaves it
   const int32_t* list = idx + size_t(blk) * P.nkb;
   const float* wl = weights + size_t(blk) * P.nkb;
   const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(

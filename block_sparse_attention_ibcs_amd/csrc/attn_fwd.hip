@@ -3,9 +3,10 @@
 // AB-Attention abstract (paperdot search page, query "Xing Ma"): exact attention
 // on the kept key/value blocks only (problem sentence); each kept block j is
 // weighted by the inverse of its inclusion probability w_j in both the softmax
-// numerator and denominator, so one pass estimates dense attention (SIP
-// sentence); key/value sub-blocks much smaller than a matrix-core tile are
-// gathered into full tiles (kernel sentence). The INTRA abstract (paperdot
+// numerator and denominator, which makes a single pass an unbiased
+// Horvitz-Thompson estimate of the dense numerator and denominator (SIP
+// sentence); kept sub-blocks, each holding far fewer keys than one matrix-core
+// tile, are packed side by side to fill whole tiles (kernel sentence). The INTRA abstract (paperdot
 // search page, query "Wenbo Lu") describes the same idea for static patterns:
 // a FlashAttention-style kernel that loads non-contiguous tokens and packs them
 // densely.
@@ -96,7 +97,8 @@ void attn_fwd_bf16(Dims P, const uint16_t* __restrict__ q, const uint16_t* __res
   const int N = P.N;
   const int row0 = i * BQ;
   const int n = min(BQ, N - row0);
-  const int cnt = counts[blk];
+  // a count outside [0, NKB] is clamped, so no list or weight read leaves the row
+  const int cnt = min(max(counts[blk], 0), P.nkb);
   const int32_t* list = idx + size_t(blk) * P.nkb;
   const float* wl = weights + size_t(blk) * P.nkb;
   // one head of K or V; rows at or beyond N read as zeros (buffer range check)
@@ -386,7 +388,7 @@ __global__ __launch_bounds__(128) void attn_fwd_f32(Dims P, const float* __restr
   const int N = P.N, Bk = P.Bk, Bq = P.Bq;
   const int row0 = i * Bq;
   const int n = min(Bq, N - row0);
-  const int cnt = counts[blk];
+  const int cnt = min(max(counts[blk], 0), P.nkb);  // clamped to the row
   const int32_t* list = idx + size_t(blk) * P.nkb;
   const float* wl = weights + size_t(blk) * P.nkb;
   const int r = threadIdx.x;
@@ -408,7 +410,7 @@ __global__ __launch_bounds__(128) void attn_fwd_f32(Dims P, const float* __restr
       float lw = -__builtin_inff();
       if (ord < cnt) {
         const int kk = list[ord] * Bk + e;
-        if (kk < N) {
+        if (kk >= 0 && kk < N) {  // entries outside the sequence contribute nothing
           key = kk;
           lw = __builtin_amdgcn_logf(wl[ord]);
         }

@@ -6,11 +6,13 @@ benchmark's CPU-baseline leg may import this package; the library under
 
 What it computes follows the AB-Attention abstract (paperdot search page,
 query "Xing Ma"): dynamic block-sparse attention that computes exact attention
-only on key/value blocks selected from the current activations (problem
-sentence), scored by clustering queries inside each query block without
-permuting tokens (IBCS sentence), sampled in proportion to those scores and
-reweighted by the inverse inclusion probability so one pass estimates dense
-attention (SIP sentence). The pages give no formulas; every constant and rule
+only on key/value blocks chosen from the current activations (problem
+sentence), scored by clustering the queries of each query block in place,
+token order untouched (IBCS sentence), drawn with probabilities proportional
+to those scores and
+given weight 1/pi (pi the block's inclusion probability), which makes one
+weighted pass an unbiased estimate of the dense numerator and denominator
+(SIP sentence). The pages give no formulas; every constant and rule
 the abstract leaves open is a stated reading, listed in the module that uses it.
 
 The INTRA relay patterns (``intra``) follow the INTRA page (paperdot search page,

@@ -3,8 +3,9 @@
 AB-Attention abstract (paperdot search page, query "Xing Ma"): 3D full
 attention is the dense target (opening sentence); dynamic block-sparse
 attention computes exact attention on the selected key/value blocks only
-(problem sentence); kept blocks are reweighted by their inverse inclusion
-probability so one pass estimates dense attention (SIP sentence).
+(problem sentence); each kept block carries weight 1/pi_j, pi_j its inclusion
+probability, so the single weighted pass is an unbiased estimate of the dense
+numerator and denominator (SIP sentence).
 
 Readings: non-causal attention with softmax scale 1/sqrt(d) and no positional
 transform inside the op; the weight omega_j multiplies block j's terms in both

@@ -139,11 +139,86 @@ def expcast_codes(y):
 EXPCAST_LOG2_TOP = 8.75  # 2^(y + 8.75) is what a code stands for: log2 of the row scale
 
 
+def dequantize(prep, q_block, k_block):
+    """The values the FP8 operands stand for, float64 [B,H,N,d] each: q = qscale of the
+    row's query block x decode(qcode), k = kscale of the key's sub-block x
+    decode(kcode), v = vmean of the key's sub-block + vscale x decode(vcode)
+    (V-Smooth reconstruction)."""
+    qc, kc, vc = prep["qcode"], prep["kcode"], prep["vcode"]
+    N = qc.shape[2]
+    rq = np.arange(N) // q_block
+    rk = np.arange(N) // k_block
+    q = prep["qscale"][:, :, rq, None].astype(np.float64) * e4m3_decode(qc)
+    k = prep["kscale"][:, :, rk, None].astype(np.float64) * e4m3_decode(kc)
+    v = prep["vmean"][:, :, rk, :].astype(np.float64) + prep["vscale"][:, :, None, None].astype(np.float64) * e4m3_decode(vc)
+    return q, k, v
+
+
+def _row_terms(prep, idx, weights, counts, q_block, k_block, scale, b, h, r):
+    """Kept key rows of query row (b, h, r) in list order, each with its sub-block's
+    position t in the list and its weighted logit in log2 units,
+      x = (qscale * kscale_j * scale * log2(e)) * (qcode . kcode) + log2(w_t),
+    computed exactly (float64)."""
+    qc, kc = prep["qcode"], prep["kcode"]
+    N = qc.shape[2]
+    i = r // q_block
+    cnt = int(counts[b, h, i])
+    c2 = float(scale) * np.log2(np.e)
+    qv = e4m3_decode(qc[b, h, r]).astype(np.float64)
+    rows, pos, xs = [], [], []
+    for t in range(cnt):
+        j = int(idx[b, h, i, t])
+        a = float(prep["qscale"][b, h, i]) * float(prep["kscale"][b, h, j]) * c2
+        lw = float(np.log2(np.float64(weights[b, h, i, t])))
+        for kk in range(k_block):
+            row = j * k_block + kk
+            if row >= N:
+                continue
+            rows.append(row)
+            pos.append(t)
+            xs.append(a * float(np.dot(qv, e4m3_decode(kc[b, h, row]).astype(np.float64))) + lw)
+    return np.array(rows, dtype=np.int64), np.array(pos, dtype=np.int64), np.array(xs, dtype=np.float64)
+
+
+def attn_rows_fp8_plain(prep, idx, weights, counts, q_block, k_block, scale, rows):
+    """FP8 weighted block-sparse attention for query rows by its plain definition
+    (VC-Attention page, ExpCast-FP8 paragraph; float64): one reference per row,
+    M = the largest weighted logit x (log2 units) over all kept keys, and every
+    probability is the E4M3 value of its ExpCast code against it,
+      p_k = decode(ExpCast(x_k - M)),   l = sum_k p_k,
+      O = (vscale * sum_k p_k decode(vcode_k) + sum_t (sum_{k in t} p_k) vmean_t) / l,
+      lse = (M + log2 l - 8.75) * ln 2,
+    with x_k as in _row_terms; O = 0 and lse = -inf for an empty list. No tiles: the
+    order in which keys are visited does not enter.
+
+    rows: iterable of (b, h, r). Returns {(b, h, r): (out float64 [d], lse float)}."""
+    vc = prep["vcode"]
+    d = vc.shape[3]
+    res = {}
+    for (b, h, r) in rows:
+        i = r // q_block
+        krows, pos, xs = _row_terms(prep, idx, weights, counts, q_block, k_block, scale, b, h, r)
+        if krows.size == 0:
+            res[(b, h, r)] = (np.zeros(d, np.float64), -np.inf)
+            continue
+        M = float(xs.max())
+        p = e4m3_decode(expcast_codes(xs - M))
+        l = float(p.sum())
+        o = float(prep["vscale"][b, h]) * (p @ e4m3_decode(vc[b, h, krows]))
+        for t in np.unique(pos):
+            j = int(idx[b, h, i, t])
+            o = o + float(p[pos == t].sum()) * prep["vmean"][b, h, j].astype(np.float64)
+        res[(b, h, r)] = (o / l, (M + np.log2(l) - EXPCAST_LOG2_TOP) * np.log(2.0))
+    return res
+
+
 def attn_rows_fp8(prep, idx, weights, counts, q_block, k_block, scale, rows, tile=64):
     """FP8 weighted block-sparse attention for query rows, computed exactly (float64)
-    from the FP8 operands, in the online form the kernel uses (our reading; the page
-    gives no algorithm): the kept sub-blocks of query block (b, h, i) are laid end to
-    end and walked in tiles of `tile` key slots; per tile, for each row
+    from the FP8 operands, in the online form the kernel uses (a reading of how the
+    codes are taken when the rows are walked in tiles; the plain definition, one
+    reference for the whole row, is attn_rows_fp8_plain): the kept sub-blocks of query
+    block (b, h, i) are laid end to end and walked in tiles of `tile` key slots; per
+    tile, for each row
       x = (qscale * kscale_j * scale * log2(e)) * (qcode . kcode) + log2(w_j)  (log2 units)
       m <- max(m, max over the tile's real keys of x); O, l rescaled by 2^(m_old - m)
       p = decode(ExpCast(x - m))                      (E4M3 values; padding keys p = 0)

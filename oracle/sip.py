@@ -1,9 +1,11 @@
 """SIP: sampling with inclusion-probability weighting (oracle side).
 
 AB-Attention abstract (paperdot search page, query "Xing Ma"), SIP sentence:
-blocks are sampled in proportion to the IBCS estimates and the kept ones are
-reweighted by the inverse of their inclusion probability, so that one pass
-estimates dense attention instead of truncating it. The pages fix neither the
+blocks are drawn with probabilities proportional to the IBCS estimates and
+each kept block carries weight 1/pi_j, pi_j its inclusion probability; the
+weighted single pass is then an unbiased (Horvitz-Thompson) estimate of the
+dense softmax numerator and denominator, where dropping the unkept blocks
+would bias both. The pages fix neither the
 sampling design nor the budget. Readings used here, all in integer arithmetic
 on the fp32 scores so that any correct implementation reproduces them bit for
 bit:

@@ -210,3 +210,122 @@ def test_attn_fp8_video_shape(name):
     nqb = -(-w.N // w.q_block)
     blocks = [(0, 0, 0), (0, 0, nqb - 1), (0, 1, 77), (0, 1, nqb - 1)]
     _check_attn(q, k, v, w.k_block, w.density, seed=11, blocks=blocks, rows_per_block=6)
+
+
+# ---- ab_attn_fwd_fp8 against the plain definition (one reference per row) -----------
+# The kernel takes each tile's codes against a running reference (raised to the tile
+# maximum when it grows); the plain definition takes every code against the row's
+# overall maximum (oracle.fp8.attn_rows_fp8_plain). Both replace each exact probability
+# a_k = 2^(y_k + 8.75) by an E4M3 value within the ExpCast factor F = 1.0616 * 2^(1/16)
+# (pinned in tests/test_oracle_fp8.py); the kernel's fp32 logits move y by less than
+# 2^-7, so its codes are within F_k = 1.0616 * 2^(1/16 + 1/128), and its keys outside
+# the normal range within 2^-6 absolutely. expcast_output_bound turns these into a
+# bound per output element around the exact weighted attention over the values the
+# FP8 operands stand for (sparse_ht_attention on the dequantised operands), so
+#   |O_kernel - O_exact| <= B(F_k) + 2^-8 |O| + 1e-4   (output rounding, fp32 sums)
+#   |O_kernel - O_plain| <= B(F_k) + B(F) + 2^-8 |O| + 1e-4
+#   |LSE_kernel - LSE_exact| <= ln F_k + 1e-3.
+F_KERNEL = 1.0616 * 2.0 ** (1 / 16 + 1 / 128)
+
+
+def _hot_first_lists(nqb, nkb, density, seed):
+    """Kept lists that always start with sub-block 0 (made to hold every row's largest
+    logit), then a seeded choice of the others; weights 1 on sub-block 0, 1..8 elsewhere."""
+    rng = np.random.default_rng(seed)
+    idx = np.zeros((1, 1, nqb, nkb), np.int32)
+    w = np.zeros((1, 1, nqb, nkb), np.float32)
+    cnt = np.zeros((1, 1, nqb), np.int32)
+    for i in range(nqb):
+        k = max(2, int(round(density * nkb)))
+        sel = np.concatenate([[0], np.sort(rng.choice(np.arange(1, nkb), k - 1, replace=False))])
+        idx[0, 0, i, :k] = sel
+        w[0, 0, i, :k] = np.concatenate([[1.0], rng.uniform(1.0, 8.0, k - 1)]).astype(np.float32)
+        cnt[0, 0, i] = k
+    return idx, w, cnt
+
+
+def _plain_case(q, k, v, bk, idx, w, cnt, rows_per_block, seed):
+    from oracle import sparse_ht_attention
+    from test_oracle_fp8 import F_EXPCAST, expcast_output_bound
+
+    dev = _gpu()
+    bq = 128
+    qd, kd, vd = (x.to(dev) for x in (q, k, v))
+    desc = ab.Desc.for_tensor(qd, bq, bk, 1)
+    N, d = q.shape[2], q.shape[3]
+    scale = desc_scale(d)
+    ops = ab.ab_fp8_prepare(desc, qd, kd, vd)
+    out, lse = ab.ab_attn_fwd_fp8(desc, ops, torch.from_numpy(idx).to(dev), torch.from_numpy(w).to(dev),
+                                  torch.from_numpy(cnt).to(dev))
+    torch.cuda.synchronize()
+    out, lse = out.float().cpu().numpy(), lse.cpu().numpy()
+    prep = fp8.prepare(q.float().numpy(), k.float().numpy(), v.float().numpy(), bq, bk)
+    qx, kx, vx = fp8.dequantize(prep, bq, bk)
+    rng = np.random.default_rng(seed)
+    rows = []
+    for i in range(desc.nqb):
+        r0, r1 = i * bq, min(N, (i + 1) * bq)
+        rows += sorted(set([r0, r1 - 1] + rng.choice(np.arange(r0, r1), min(rows_per_block, r1 - r0), replace=False).tolist()))
+    plain = fp8.attn_rows_fp8_plain(prep, idx, w, cnt, bq, bk, scale, [(0, 0, r) for r in rows])
+    stats = {"exact": 0.0, "plain": 0.0, "plain_abs": 0.0}
+    for r in rows:
+        i = r // bq
+        c = int(cnt[0, 0, i])
+        sel, wt = idx[0, 0, i, :c], w[0, 0, i, :c]
+        o_ex, lse_ex = sparse_ht_attention(qx[0, 0, r:r + 1], kx[0, 0], vx[0, 0], sel, wt, bk, scale)
+        keys = np.concatenate([np.arange(j * bk, min(N, (j + 1) * bk)) for j in sel])
+        lw = np.concatenate([np.full(min(N, (j + 1) * bk) - j * bk, np.log(float(x))) for j, x in zip(sel, wt)])
+        logits = scale * (kx[0, 0, keys] @ qx[0, 0, r]) + lw
+        b_k = expcast_output_bound(logits, vx[0, 0, keys], o_ex[0], F=F_KERNEL, small=2.0 ** -6)
+        b_p = expcast_output_bound(logits, vx[0, 0, keys], o_ex[0], F=F_EXPCAST)
+        got = out[0, 0, r]
+        slack = 2.0 ** -8 * np.abs(o_ex[0]) + 1e-4
+        e_ex = np.abs(got - o_ex[0])
+        e_pl = np.abs(got - plain[(0, 0, r)][0])
+        assert np.all(e_ex <= b_k + slack), (r, float((e_ex / (b_k + slack)).max()))
+        assert np.all(e_pl <= b_k + b_p + slack), (r, float((e_pl / (b_k + b_p + slack)).max()))
+        assert abs(lse[0, 0, r] - lse_ex[0]) <= np.log(F_KERNEL) + 1e-3, r
+        stats["exact"] = max(stats["exact"], float((e_ex / (b_k + slack)).max()))
+        stats["plain"] = max(stats["plain"], float((e_pl / (b_k + b_p + slack)).max()))
+        stats["plain_abs"] = max(stats["plain_abs"], float(e_pl.max()))
+    return out, plain, rows, stats
+
+
+@pytest.mark.parametrize("bk", [16, 32])
+def test_attn_fp8_within_expcast_bound_of_plain_definition(bk):
+    """Weighted lists (weights 1..8), several tiles per row: the kernel is within the
+    derived ExpCast bound of the exact weighted attention and of the plain definition."""
+    q, k, v = _bf16_inputs((1, 1, 640, 128), seed=40 + bk, offset=1.0)
+    nqb, nkb = 5, 640 // bk
+    idx, w, cnt = _lists(1, 1, nqb, nkb, 0.5, seed=bk)
+    _, _, _, stats = _plain_case(q, k, v, bk, idx, w, cnt, rows_per_block=24, seed=bk)
+    print(f"bk={bk}: largest error / bound: vs exact {stats['exact']:.3f}, vs plain {stats['plain']:.3f}; "
+          f"largest |kernel - plain| {stats['plain_abs']:.4f}")
+
+
+def test_attn_fp8_matches_plain_definition_when_first_tile_holds_the_maximum():
+    """Lists whose first sub-block holds every row's largest weighted logit: the running
+    reference starts at the row maximum, so the kernel's codes are those of the plain
+    definition (up to a code step at an fp32 rounding boundary), and the kernel is held to
+    the tight bound of the tiled comparison against attn_rows_fp8_plain."""
+    g = torch.Generator().manual_seed(17)
+    N, d, bk = 512, 128, 32
+    u = torch.randn(d, generator=g)
+    u = u / u.norm()
+    q = (4.0 * u + 0.5 * torch.randn((1, 1, N, d), generator=g)).to(torch.bfloat16)
+    k = (0.5 * torch.randn((1, 1, N, d), generator=g))
+    k[0, 0, :bk] += 32.0 * u
+    k = k.to(torch.bfloat16)
+    v = torch.randn((1, 1, N, d), generator=g).to(torch.bfloat16)
+    nqb, nkb = N // 128, N // bk
+    idx, w, cnt = _hot_first_lists(nqb, nkb, 0.5, seed=3)
+    out, plain, rows, _ = _plain_case(q, k, v, bk, idx, w, cnt, rows_per_block=128, seed=3)
+    # the premise: sub-block 0 holds every checked row's largest weighted logit
+    prep = fp8.prepare(q.float().numpy(), k.float().numpy(), v.float().numpy(), 128, bk)
+    for r in rows:
+        krows, _, xs = fp8._row_terms(prep, idx, w, cnt, 128, bk, desc_scale(d), 0, 0, r)
+        assert krows[int(np.argmax(xs))] < bk, r
+    o_ref = np.stack([plain[(0, 0, r)][0] for r in rows])
+    got = out[0, 0, rows]
+    assert np.all(np.abs(got - o_ref) <= TOL_ABS + TOL_REL * np.abs(o_ref))
+    assert np.linalg.norm(got - o_ref) / np.linalg.norm(o_ref) <= TOL_RL2

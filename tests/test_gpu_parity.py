@@ -7,9 +7,10 @@ inputs -
   sampler run by the oracle on the GPU's own scores: idx, weights, counts and
   mask bits bit-exact;
   attention run by the oracle on the GPU's own idx/weights, against the exact
-  (float64) result: |error| <= 2e-2 plus half an output ulp (2^-8 |O| for bf16)
-  elementwise and relative L2 <= 1e-2 (bf16); 1e-5 (fp32); LSE within 1e-3
-  (bf16) or 1e-5 (fp32) relative to max(1, |LSE|).
+  (float64) result: |error| <= 2e-2 + 2^-8 |O| elementwise (2^-8 |O| is the
+  largest half-ulp of a bf16 value of magnitude |O|; the elements beyond the plain
+  2e-2 are counted and printed) and relative L2 <= 1e-2 (bf16); 1e-5 + 2^-24 |O|
+  and 1e-5 (fp32); LSE within 1e-3 (bf16) or 1e-5 (fp32) relative to max(1, |LSE|).
 The four video-shaped workloads run at full size in the launch configuration
 the benchmark times; the oracle checks a seeded sample of query blocks that
 always includes the first block and the ragged last one, and properties that
@@ -155,6 +156,9 @@ def check_sampler_any_size(run):
         assert np.all(run.wts[b, h, i, :c] >= 1.0)
 
 
+STRICT = {"elements": 0, "beyond_plain_bound": 0}  # elements past the plain o_abs bound
+
+
 def check_attention(run, blocks):
     w = run.w
     tol = TOL[w.dtype]
@@ -170,6 +174,8 @@ def check_attention(run, blocks):
             continue
         err = np.abs(got - o_ref)
         assert np.all(err <= o_bound(o_ref, tol)), (b, h, i, float(err.max()))
+        STRICT["elements"] += err.size
+        STRICT["beyond_plain_bound"] += int((err > tol["o_abs"]).sum())
         rl2 = np.linalg.norm(got - o_ref) / max(np.linalg.norm(o_ref), 1e-30)
         assert rl2 <= tol["o_rl2"], (b, h, i, rl2)
         lerr = np.abs(run.lse[b, h, lo:hi] - lse_ref) / np.maximum(1.0, np.abs(lse_ref))
@@ -242,7 +248,8 @@ def test_video_workload_full_path(name):
     # realised density is close to the target (Poisson sampling around K per row)
     K = max(1, min(w.nkb, math.floor(run.density * w.nkb + 0.5)))
     assert abs(run.cnt.mean() - K) < 0.05 * K + 1
-    print(f"{name}: worst attention |err| {worst:.3e}, mean kept {run.cnt.mean():.1f} of K={K}")
+    print(f"{name}: worst attention |err| {worst:.3e}, mean kept {run.cnt.mean():.1f} of K={K}; "
+          f"elements past the plain 2e-2 so far: {STRICT['beyond_plain_bound']} of {STRICT['elements']}")
 
 
 class _ScoreRows:

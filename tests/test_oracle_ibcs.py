@@ -3,7 +3,7 @@
 * P2 - one cluster per query: the estimate equals the brute-force block mass of
   the dense softmax, averaged over the block's queries.
 * P3 - one cluster: the estimate equals the block softmax mass of the block's
-  mean query (the pooled "coarse summary").
+  mean query (the pooled summary the problem sentence criticises).
 * P4 - k-means invariants: centroids are the means of their members; the
   objective does not increase; assignments are nearest-centroid; T iterations
   are taken; the result matches scikit-learn's Lloyd iterations from the same
