@@ -193,3 +193,37 @@ def block_scores(mu, sizes, n_rows, K, k_block, scale, bf16):
     w = np.asarray(sizes, dtype=np.float64) / float(n_rows)
     s = (w[:, None] * np.exp(ell - L[:, None])).sum(axis=0)
     return s.astype(np.float32)
+
+
+def block_scores_many(mu, sizes, n_rows, K, k_block, scale, bf16, chunk=64):
+    """block_scores for many query blocks of one head at once (the same definition, the
+    centroids of several blocks stacked into one matrix product).
+
+    mu: float32 [nb, C, d]; sizes: [nb, C]; n_rows: [nb] rows per block; K: [N, d] keys.
+    Returns float32 [nb, NKB]. chunk: blocks per matrix product (memory bound only)."""
+    mu = np.asarray(mu, dtype=np.float32)
+    nb, C, d = mu.shape
+    K = np.asarray(K, dtype=np.float64)
+    N = K.shape[0]
+    nkb = -(-N // k_block)
+    pad = nkb * k_block - N
+    out = np.zeros((nb, nkb), np.float32)
+    if bf16:
+        c2 = np.float32(np.float32(scale) * np.float32(np.log2(np.e)))
+    for b0 in range(0, nb, chunk):
+        m = mu[b0:b0 + chunk]
+        nbc = m.shape[0]
+        flat = m.reshape(nbc * C, d)
+        if bf16:
+            logits = np.log(2.0) * (round_bf16((flat * c2).astype(np.float32)).astype(np.float64) @ K.T)
+        else:
+            logits = float(scale) * (flat.astype(np.float64) @ K.T)
+        if pad:
+            logits = np.concatenate([logits, np.full((logits.shape[0], pad), -np.inf)], axis=1)
+        ell = _logsumexp(logits.reshape(nbc * C, nkb, k_block), axis=2)  # [nbc*C, NKB]
+        L = _logsumexp(ell, axis=1)
+        w = np.asarray(sizes[b0:b0 + chunk], dtype=np.float64).reshape(nbc * C) / np.repeat(
+            np.asarray(n_rows[b0:b0 + chunk], dtype=np.float64), C)
+        s = (w[:, None] * np.exp(ell - L[:, None])).reshape(nbc, C, nkb).sum(axis=1)
+        out[b0:b0 + nbc] = s.astype(np.float32)
+    return out

@@ -18,6 +18,8 @@ hold at any size are checked on every row.
 """
 
 import math
+import os
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import pytest
@@ -27,6 +29,8 @@ import block_sparse_attention_ibcs_amd as ab
 import workloads
 from oracle import (Params, block_scores, dense_attention, kmeans_fp32, round_bf16, sample_rows,
                     sample_rows_systematic, sparse_ht_attention, topk_rows)
+from oracle import native
+from oracle.ibcs import block_scores_many
 from oracle.intra import default_partition, intra_lists, intra_row_order
 from oracle.sip import SIP_ONE
 
@@ -184,6 +188,107 @@ def check_attention(run, blocks):
     return worst
 
 
+# ---------------------------------------------------------- every row, full size
+# The C twin of the oracle's clustering and sampler (oracle/native.py, pinned to the
+# numpy forms in tests/test_oracle_native.py) makes it possible to check every query
+# block and every score row of the full-size workloads.
+
+_THREADS = min(16, os.cpu_count() or 1)
+
+
+def check_kmeans_every_block(run):
+    """Centroids, sizes and assignments of every query block of every head, bit-exact."""
+    w = run.w
+    cent, sizes, assign = ab.ab_score_debug(run.desc, run.qd)
+    torch.cuda.synchronize()
+    cent, sizes, assign = cent.cpu().numpy(), sizes.cpu().numpy(), assign.cpu().numpy()
+    mu, sz, a = native.kmeans_all(run.q, w.q_block, w.n_clusters, w.kmeans_iters)
+    bad = np.argwhere(np.any(cent.view(np.uint32) != mu.view(np.uint32), axis=(-2, -1)))
+    assert bad.size == 0, ("centroids differ", bad[:5].tolist())
+    assert np.array_equal(sizes, sz)
+    assert np.array_equal(assign, a)
+    return mu, sz
+
+
+def check_sampler_every_row(scores, density, seed, idx, wts, cnt, mask=None, tag=""):
+    """The sampler twin on the GPU's own scores reproduces the GPU's counts, kept
+    indices, weights and mask bits on every row, bit for bit."""
+    ref = native.sample_all(scores, density, seed)
+    assert np.array_equal(cnt, ref["counts"]), (tag, "counts")
+    valid = np.arange(scores.shape[-1]) < cnt[..., None]
+    assert np.array_equal(np.where(valid, idx, 0), np.where(valid, ref["idx"], 0)), (tag, "idx")
+    assert np.array_equal(np.where(valid, wts.view(np.uint32), 0), np.where(valid, ref["weight"].view(np.uint32), 0)), \
+        (tag, "weights")
+    if mask is not None:
+        assert np.array_equal(mask, ref["mask"]), (tag, "mask")
+    return int(cnt.size)
+
+
+def check_attention_heads(run, heads):
+    """Attention on every query block of the given heads against the oracle on the GPU's
+    own lists (float64 keys and values prepared once per head; blocks in parallel)."""
+    w = run.w
+    tol = TOL[w.dtype]
+    worst = 0.0
+    for (b, h) in heads:
+        k64 = run.k[b, h].astype(np.float64)
+        v64 = run.v[b, h].astype(np.float64)
+
+        def one(i):
+            lo, hi = _rows_of(w, b, h, i)
+            c = int(run.cnt[b, h, i])
+            o_ref, lse_ref = sparse_ht_attention(run.q[b, h, lo:hi], k64, v64, run.idx[b, h, i, :c],
+                                                 run.wts[b, h, i, :c], w.k_block, run.scale)
+            got = run.out[b, h, lo:hi].astype(np.float64)
+            if c == 0:
+                return (i, bool(np.all(got == 0) and np.all(np.isneginf(run.lse[b, h, lo:hi]))), 0.0, 0)
+            err = np.abs(got - o_ref)
+            ok = bool(np.all(err <= o_bound(o_ref, tol)))
+            ok &= np.linalg.norm(got - o_ref) / max(np.linalg.norm(o_ref), 1e-30) <= tol["o_rl2"]
+            lerr = np.abs(run.lse[b, h, lo:hi] - lse_ref) / np.maximum(1.0, np.abs(lse_ref))
+            ok &= bool(lerr.max() <= tol["lse"])
+            return (i, ok, float(err.max()), int((err > tol["o_abs"]).sum()))
+
+        with ThreadPoolExecutor(_THREADS) as ex:
+            res = list(ex.map(one, range(w.nqb)))
+        failed = [i for (i, ok, _, _) in res if not ok]
+        assert not failed, ((b, h), failed[:10])
+        worst = max([worst] + [e for (_, _, e, _) in res])
+        STRICT["elements"] += len(res) * w.q_block * w.d
+        STRICT["beyond_plain_bound"] += sum(x for (_, _, _, x) in res)
+    return worst
+
+
+def check_independent_masks(run, heads, mu_all, sz_all):
+    """P10: scores computed on the CPU from the CPU clustering, sampled on the CPU,
+    against the GPU's end-to-end masks on every row of the given heads. Where the two
+    differ, the 24-bit uniform must lie between the CPU and GPU thresholds (the flip is
+    the score difference showing), and the number of flips must stay within the
+    Poisson range of its expectation, the sum over blocks of |t_cpu - t_gpu| / 2^24.
+    The CPU scores are also within the score tolerance of the GPU's on every row."""
+    w = run.w
+    tol = TOL[w.dtype]
+    n_rows = np.array([min(w.q_block, w.N - i * w.q_block) for i in range(w.nqb)])
+    s_cpu = np.stack([block_scores_many(mu_all[b, h], sz_all[b, h], n_rows, run.k[b, h], w.k_block, run.scale,
+                                        w.dtype == "bf16") for (b, h) in heads])
+    s_gpu = np.stack([run.scores[b, h] for (b, h) in heads])
+    lim = tol["score_abs"] + tol["score_rel"] * np.abs(s_cpu.astype(np.float64))
+    assert np.all(np.abs(s_gpu.astype(np.float64) - s_cpu) <= lim)
+    cpu = native.sample_all(s_cpu, run.density, run.seed, with_thresholds=True, with_uniforms=True, heads=heads)
+    gpu = native.sample_all(s_gpu, run.density, run.seed, with_thresholds=True, heads=heads)
+    gpu_mask = np.stack([run.mask[b, h] for (b, h) in heads])
+    assert np.array_equal(gpu["mask"], gpu_mask)  # the stage-injected equality, as above
+    nkb = w.nkb
+    flip = np.unpackbits((cpu["mask"] ^ gpu_mask).view(np.uint8), axis=-1, bitorder="little")[..., :nkb].astype(bool)
+    t_c, t_g, u = cpu["thresh"].astype(np.int64), gpu["thresh"].astype(np.int64), cpu["uniforms"].astype(np.int64)
+    explained = (np.minimum(t_c, t_g) <= u) & (u < np.maximum(t_c, t_g))
+    assert np.all(explained[flip]), "a mask flip that no threshold difference explains"
+    expected = float(np.abs(t_c - t_g).sum()) / SIP_ONE
+    flips = int(flip.sum())
+    assert flips <= expected + 5.0 * math.sqrt(expected) + 3, (flips, expected)
+    return flips, expected, int(flip.size)
+
+
 _CACHE = {}
 
 
@@ -233,22 +338,31 @@ def test_tiny_end_to_end_masks_match_oracle():
 
 @pytest.mark.parametrize("name", ["wan1.3b", "hunyuan", "wan14b"])
 def test_video_workload_full_path(name):
+    """Full size, in the benchmark's launch configuration: k-means bit-exact on every
+    query block of every head; the sampler bit-exact on every score row; scores against
+    the oracle on sampled blocks and as distributions on every row; attention against
+    the oracle on every query block of the first and the last head, and on sampled
+    blocks of the others; independent CPU masks (P10) on every row of the first and
+    last head (all heads of the 12-head shape)."""
     run = _run(name)
-    blocks = run.blocks(24)
-    check_kmeans(run, blocks)
-    check_scores(run, blocks)
-    rng = np.random.default_rng(11)
-    rows = set(blocks)
     w = run.w
-    for t in rng.choice(w.B * w.H * w.nqb, size=200, replace=False):
-        rows.add((int(t) // (w.H * w.nqb), (int(t) // w.nqb) % w.H, int(t) % w.nqb))
-    check_sampler(run, sorted(rows))
+    blocks = run.blocks(24)
+    mu_all, sz_all = check_kmeans_every_block(run)
+    check_scores(run, blocks)
+    rows = check_sampler_every_row(run.scores, run.density, run.seed, run.idx, run.wts, run.cnt, run.mask, tag=name)
     check_sampler_any_size(run)
-    worst = check_attention(run, blocks)
+    heads = [(0, 0), (w.B - 1, w.H - 1)]
+    worst = check_attention_heads(run, heads)
+    worst = max(worst, check_attention(run, [x for x in blocks if (x[0], x[1]) not in heads]))
+    p10_heads = [(b, h) for b in range(w.B) for h in range(w.H)] if w.H <= 12 else heads
+    flips, expected, entries = check_independent_masks(run, p10_heads, mu_all, sz_all)
     # realised density is close to the target (Poisson sampling around K per row)
     K = max(1, min(w.nkb, math.floor(run.density * w.nkb + 0.5)))
     assert abs(run.cnt.mean() - K) < 0.05 * K + 1
-    print(f"{name}: worst attention |err| {worst:.3e}, mean kept {run.cnt.mean():.1f} of K={K}; "
+    print(f"{name}: k-means bit-exact on {w.B * w.H * w.nqb} blocks, sampler bit-exact on {rows} rows; "
+          f"attention on every block of {len(heads)} heads, worst |err| {worst:.3e}; "
+          f"independent masks: {flips} flips in {entries} entries (expected {expected:.2f}); "
+          f"mean kept {run.cnt.mean():.1f} of K={K}; "
           f"elements past the plain 2e-2 so far: {STRICT['beyond_plain_bound']} of {STRICT['elements']}")
 
 
@@ -268,9 +382,9 @@ def test_gather_sweep_shape(bk):
     """Gather-cost sweep on the 40-head, 75600-token shape: for one key sub-block size the
     scorer once, then sampler and attention at densities 1, 0.25, 0.10 and 0.05. On
     sampled query blocks (the first, the ragged last, one inside) the scores are within
-    tolerance, the draw is bit-exact, the output matches the oracle on the GPU's own
-    lists, and at density 1 every sub-block is kept and the output equals dense
-    attention."""
+    tolerance, the output matches the oracle on the GPU's own lists, and at density 1
+    every sub-block is kept and the output equals dense attention; the draw is
+    bit-exact on every row of every point."""
     run = _run("wan14b")
     w = run.w
     tol = TOL["bf16"]
@@ -280,6 +394,7 @@ def test_gather_sweep_shape(bk):
     scores_d = ab.ab_score(desc, run.qd, run.kd)
     torch.cuda.synchronize()
     srows = _ScoreRows(scores_d, blocks)
+    scores_all = scores_d.cpu().numpy()
     for (b, h, i) in blocks:
         lo, hi = _rows_of(w, b, h, i)
         mu, sz, _ = kmeans_fp32(run.q[b, h, lo:hi], w.n_clusters, w.kmeans_iters)
@@ -292,6 +407,9 @@ def test_gather_sweep_shape(bk):
         torch.cuda.synchronize()
         if rho == 1.0:
             assert int(cnt_d.min().item()) == nkb
+        # every row: the sampler twin on the GPU's scores, bit for bit
+        check_sampler_every_row(scores_all, rho, 3, idx_d.cpu().numpy(), wts_d.cpu().numpy(), cnt_d.cpu().numpy(),
+                                mask_d.cpu().numpy().view(np.uint32), tag=(bk, rho))
         ref = sample_rows(srows, rho, 3, blocks)
         for (b, h, i), o in ref.items():
             c = int(cnt_d[b, h, i].item())
@@ -414,6 +532,44 @@ def test_edge_shapes(N, H, d, Bq, Bk, C, T, density):
             err = np.abs(run.out[0, h] - o)
             assert np.all(err <= o_bound(o, TOL["bf16"]))
             assert np.linalg.norm(run.out[0, h] - o) / np.linalg.norm(o) <= 1e-2
+
+
+FP32_SHAPES = [
+    # (N, H, d, Bq, Bk, C, T, density): float32 inputs through every stage
+    (300, 2, 128, 128, 32, 8, 4, 0.3),
+    (300, 1, 128, 64, 16, 4, 2, 0.4),
+    (257, 2, 64, 128, 64, 8, 3, 0.5),
+    (200, 1, 128, 128, 128, 8, 4, 1.0),
+    (190, 1, 64, 64, 16, 64, 2, 0.25),
+    (333, 1, 128, 128, 16, 128, 1, 0.2),
+]
+
+
+@pytest.mark.parametrize("N,H,d,Bq,Bk,C,T,density", FP32_SHAPES)
+def test_fp32_shapes(N, H, d, Bq, Bk, C, T, density):
+    """Float32 inputs at both head dims and both query block sizes, every key sub-block
+    size: k-means bit-exact, scores within 1e-6 + 1e-4 s, the draw bit-exact, attention
+    within 1e-5 of the oracle, on every block; at density 1 the output equals dense
+    attention within 1e-5."""
+    _gpu()
+    w = workloads.Workload("fp32", 1, H, (1, 1, N), d, "fp32", Bq, Bk, C, density, 0.5, False, kmeans_iters=T)
+    rng = np.random.default_rng(N * 7 + d + Bk)
+    base = rng.standard_normal((1, H, N, d)).astype(np.float32)
+    q = (base + 0.5 * rng.standard_normal((1, H, N, d))).astype(np.float32)
+    k = (base + 0.5 * rng.standard_normal((1, H, N, d))).astype(np.float32)
+    v = rng.standard_normal((1, H, N, d)).astype(np.float32)
+    run = Run(w, inputs=(q, k, v), seed=2)
+    blocks = run.blocks(64)
+    check_kmeans(run, blocks)
+    check_scores(run, blocks)
+    check_sampler(run, blocks)
+    check_sampler_any_size(run)
+    check_attention(run, blocks)
+    if density == 1.0:
+        for h in range(H):
+            o, lse = dense_attention(q[0, h], k[0, h], v[0, h], run.scale)
+            assert np.abs(run.out[0, h] - o).max() <= 1e-5
+            assert np.abs(run.lse[0, h] - lse).max() <= 1e-5
 
 
 def _reference_path_inputs():

@@ -258,3 +258,28 @@ def test_kmeans_distance_uses_fused_multiply_add(dim):
     assert fused != separate
     _, _, assign = kmeans_fp32(X, 2, 1)
     assert int(assign[row]) == fused
+
+
+def test_block_scores_many_equals_block_scores():
+    """The batched form used by the full-size checks is the same definition: per block
+    it equals block_scores up to the last bit of the fp32 result (matrix products of
+    different shapes may sum in another order)."""
+    from oracle.ibcs import block_scores_many
+
+    rng = np.random.default_rng(11)
+    N, d = 700, 64
+    K = rng.standard_normal((N, d)).astype(np.float32)
+    Q = rng.standard_normal((N, d)).astype(np.float32)
+    mus, szs, ns = [], [], []
+    for i in range(6):
+        lo, hi = i * 128, min(N, (i + 1) * 128)
+        mu, sz, _ = kmeans_fp32(Q[lo:hi], 8, 2)
+        mus.append(mu)
+        szs.append(sz)
+        ns.append(hi - lo)
+    for bf in (True, False):
+        many = block_scores_many(np.stack(mus), np.stack(szs), np.array(ns), K, 32, 0.125, bf, chunk=4)
+        for i in range(6):
+            one = block_scores(mus[i], szs[i], ns[i], K, 32, 0.125, bf)
+            ulp = np.spacing(np.maximum(np.abs(one), np.float32(1e-30)))
+            assert np.all(np.abs(one - many[i]) <= ulp), (bf, i)
