@@ -29,6 +29,7 @@ __all__ = [
     "ab_abi_version",
     "ab_score_workspace_size",
     "ab_score",
+    "ab_score_noalloc",
     "ab_score_debug",
     "ab_sample",
     "ab_sample_systematic",
@@ -57,6 +58,7 @@ EXPORTED_SYMBOLS = (
     "ab_last_error",
     "ab_score_workspace_size",
     "ab_score",
+    "ab_score_noalloc",
     "ab_score_debug",
     "ab_sample",
     "ab_sample_systematic",
@@ -155,6 +157,8 @@ def load_library():
     lib.ab_score_workspace_size.argtypes = [D]
     lib.ab_score.restype = ctypes.c_int32
     lib.ab_score.argtypes = [D, P, P, P, P, ctypes.c_size_t, P]
+    lib.ab_score_noalloc.restype = ctypes.c_int32
+    lib.ab_score_noalloc.argtypes = [D, P, P, P, P]
     lib.ab_score_debug.restype = ctypes.c_int32
     lib.ab_score_debug.argtypes = [D, P, P, P, P, P]
     lib.ab_sample.restype = ctypes.c_int32
@@ -241,6 +245,23 @@ def ab_score(desc: Desc, q, k, scores=None, workspace=None, stream=None):
     rc = lib.ab_score(ctypes.byref(cd), _ptr(q), _ptr(k), _ptr(scores), _ptr(workspace), workspace.numel(),
                       _stream(stream))
     _check(rc, "ab_score")
+    return scores
+
+
+AB_SCORE_NOALLOC_SCRATCH_BYTES = 256 << 20  # the library's fixed scratch for ab_score_noalloc, per GPU
+
+
+def ab_score_noalloc(desc: Desc, q, k, scores, stream=None):
+    """IBCS scores into a caller-given fp32 [B, H, NQB, NKB] tensor, with the library's
+    fixed scratch instead of a workspace (no device allocation in the call)."""
+    lib = load_library()
+    shp = (desc.B, desc.H, desc.N, desc.d)
+    _need(q, "q", shp, desc.torch_dtype)
+    _need(k, "k", shp, desc.torch_dtype)
+    _need(scores, "scores", (desc.B, desc.H, desc.nqb, desc.nkb), torch.float32)
+    cd = desc.c()
+    rc = lib.ab_score_noalloc(ctypes.byref(cd), _ptr(q), _ptr(k), _ptr(scores), _stream(stream))
+    _check(rc, "ab_score_noalloc")
     return scores
 
 

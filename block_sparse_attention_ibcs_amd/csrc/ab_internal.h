@@ -58,6 +58,8 @@ struct ScoreWs {
 };
 
 ScoreWs score_ws_layout(const Dims& D, int num_cus);
+// the same carve-up with a given key split length (a multiple of 128)
+ScoreWs score_ws_layout_split(const Dims& D, int split_keys);
 
 // Launchers: return hipSuccess or the launch error.
 hipError_t launch_kmeans(const Dims& D, const void* q, float* centroids, uint16_t* centroids_bf16,

@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "ab_internal.h"
 
@@ -100,6 +101,36 @@ int budget_blocks(double density, int nkb) {
   return int(K);
 }
 
+// Scratch of the allocation-free scorer: a fixed device array in the library's code
+// object (each GPU the library runs on holds its own copy until the process ends).
+// Host code never passes this name to a kernel or a copy: it is a host-side stand-in;
+// the device address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kScratchBytes = AB_SCORE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` on each device, once resolved
+
+// Device address of this device's scratch array, resolved on the first call on the
+// device with that device current.
+int32_t scratch_for_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(AB_ERR_DEVICE, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(AB_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return AB_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -154,6 +185,67 @@ int32_t ab_score(const ab_desc* desc, const void* q, const void* k, float* score
   if (e != hipSuccess) return hip_fail(e, "score log-sum-exp launch");
   e = ab::launch_score_assemble(P, L, ell, lpart, sz, scores, s);
   if (e != hipSuccess) return hip_fail(e, "score assembly launch");
+  return AB_OK;
+}
+
+int32_t ab_score_noalloc(const ab_desc* desc, const void* q, const void* k, float* scores, void* stream) {
+  g_err[0] = 0;
+  ab::Dims P;
+  int32_t rc = make_dims(desc, &P);
+  if (rc) return rc;
+  if (!q || !k || !scores) return fail(AB_ERR_NULL, "q, k and scores must be non-NULL");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(scores, 4)) return fail(AB_ERR_SHAPE, "q and k must be 16-byte aligned");
+  // Heads are independent through the scorer, so the problem runs in chunks of heads
+  // that each fit the scratch array. Every chunk uses the key splits the whole problem
+  // would use, so each head's arithmetic, and its result, is the same as in ab_score.
+  const ab::ScoreWs full = ab::score_ws_layout(P, 256);
+  const int heads = P.B * P.H;
+  int per_chunk = 0;
+  for (int hc = heads; hc >= 1; hc = hc > 1 ? (hc + 1) / 2 : 0) {
+    ab::Dims Pc = P;
+    Pc.B = 1;
+    Pc.H = hc;
+    if (ab::score_ws_layout_split(Pc, full.split_keys).total <= kScratchBytes) {
+      per_chunk = hc;
+      break;
+    }
+  }
+  if (per_chunk == 0) {
+    ab::Dims P1 = P;
+    P1.B = 1;
+    P1.H = 1;
+    return fail(AB_ERR_WORKSPACE, "one head needs %zu bytes of scratch; the allocation-free scorer holds %zu",
+                ab::score_ws_layout_split(P1, full.split_keys).total, kScratchBytes);
+  }
+  if ((rc = check_device())) return rc;
+  void* base = nullptr;
+  if ((rc = scratch_for_current_device(&base))) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t esize = P.bf16 ? 2 : 4;
+  const size_t head_elems = size_t(P.N) * P.d;
+  const size_t head_scores = size_t(P.nqb) * P.nkb;
+  for (int h0 = 0; h0 < heads; h0 += per_chunk) {
+    ab::Dims Pc = P;
+    Pc.B = 1;
+    Pc.H = heads - h0 < per_chunk ? heads - h0 : per_chunk;
+    const ab::ScoreWs L = ab::score_ws_layout_split(Pc, full.split_keys);
+    unsigned char* w = static_cast<unsigned char*>(base);
+    float* cf = reinterpret_cast<float*>(w + L.centroids_f32);
+    uint16_t* cb = reinterpret_cast<uint16_t*>(w + L.centroids_bf16);
+    int32_t* sz = reinterpret_cast<int32_t*>(w + L.sizes);
+    float* ell = reinterpret_cast<float*>(w + L.ell);
+    float* lpart = reinterpret_cast<float*>(w + L.lpart);
+    const void* qc = static_cast<const unsigned char*>(q) + size_t(h0) * head_elems * esize;
+    const void* kc = static_cast<const unsigned char*>(k) + size_t(h0) * head_elems * esize;
+    float* sc = scores + size_t(h0) * head_scores;
+    hipError_t e = ab::launch_kmeans(Pc, qc, cf, Pc.bf16 ? cb : nullptr, sz, nullptr, s);
+    if (e != hipSuccess) return hip_fail(e, "k-means launch");
+    e = ab::launch_score_lse(Pc, L, kc, Pc.bf16 ? static_cast<const void*>(cb) : static_cast<const void*>(cf), ell,
+                             lpart, s);
+    if (e != hipSuccess) return hip_fail(e, "score log-sum-exp launch");
+    e = ab::launch_score_assemble(Pc, L, ell, lpart, sz, sc, s);
+    if (e != hipSuccess) return hip_fail(e, "score assembly launch");
+  }
   return AB_OK;
 }
 

@@ -378,8 +378,15 @@ ScoreWs score_ws_layout(const Dims& D, int num_cus) {
       }
     }
   }
-  int split_keys = ceil_div(ceil_div(D.N, splits), 128) * 128;
-  splits = ceil_div(D.N, split_keys);
+  const int split_keys = ceil_div(ceil_div(D.N, splits), 128) * 128;
+  return score_ws_layout_split(D, split_keys);
+}
+
+ScoreWs score_ws_layout_split(const Dims& D, int split_keys) {
+  ScoreWs L{};
+  auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
+  const size_t heads = size_t(D.B) * D.H;
+  const int splits = ceil_div(D.N, split_keys);
   L.splits = splits;
   L.split_keys = split_keys;
   size_t off = 0;

@@ -117,6 +117,26 @@ int32_t ab_score(const ab_desc* desc, const void* q, const void* k, float* score
                  void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): ab_score with no
+ * workspace argument. Its scratch is a fixed device array inside the library,
+ * AB_SCORE_NOALLOC_SCRATCH_BYTES (256 MiB) per GPU, held from the library's first
+ * kernel launch on that GPU until the process ends; its address is looked up once
+ * per device. It calls no allocating routine.
+ *
+ * Heads run in chunks that fit the scratch, each with the key splits the whole
+ * problem would use in ab_score, so the scores are bit-identical to ab_score's.
+ * A descriptor whose single head needs more scratch than the array holds is
+ * rejected with AB_ERR_WORKSPACE before anything is enqueued (ab_last_error gives
+ * both sizes). Every call on one GPU shares that GPU's array and leaves its last
+ * contents there; calls that overlap on one GPU (different streams or threads)
+ * race on it and must be ordered by the caller. Arguments and results are those
+ * of ab_score.
+ */
+#define AB_SCORE_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+int32_t ab_score_noalloc(const ab_desc* desc, const void* q, const void* k, float* scores, void* stream);
+
+/*
  * The k-means stage of ab_score on its own, with every intermediate exposed
  * (the clustering of the IBCS sentence).
  *

@@ -230,3 +230,19 @@ def test_attn_fwd_ordered_validation():
     a[0] = ctypes.c_void_p(256 + 8)
     assert lib.ab_attn_fwd_ordered(ctypes.byref(cd), *a, None, None) == -2
     assert lib.ab_attn_fwd_ordered(ctypes.byref(_desc(d=96).c()), *args, None, None) == -2
+
+
+def test_score_noalloc_host_validation():
+    """ab_score_noalloc checks its arguments on the host: NULL pointers, a bad
+    descriptor, and a head that needs more scratch than the library's fixed array
+    (rejected before any device call, so this runs without a GPU)."""
+    lib = ab.load_library()
+    good = ab.Desc(1, 2, 1000, 128, ab.AB_BF16, 128, 32, 8).c()
+    fake = ctypes.c_void_p(4096)
+    assert lib.ab_score_noalloc(ctypes.byref(good), None, fake, fake, None) == -1
+    bad = ab.Desc(1, 2, 1000, 96, ab.AB_BF16, 128, 32, 8).c()
+    assert lib.ab_score_noalloc(ctypes.byref(bad), fake, fake, fake, None) == -2
+    big = ab.Desc(1, 1, 1 << 20, 128, ab.AB_BF16, 128, 16, 8).c()
+    assert lib.ab_score_noalloc(ctypes.byref(big), fake, fake, fake, None) == -6
+    msg = lib.ab_last_error().decode()
+    assert "allocation-free" in msg and str(256 << 20) in msg
