@@ -50,6 +50,17 @@ def parse_args():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="wall time budget of the CPU oracle sample")
+    ap.add_argument("--cpu-precision", default="fp32", choices=("fp32", "fp64"),
+                    help="arithmetic of the timed CPU oracle: its fp32 timing mode (default) or its fp64 parity mode")
+    ap.add_argument("--cold-steps", type=int, default=20,
+                    help="steps timed with the caches flushed before each (a 512 MB buffer written between steps)")
+    ap.add_argument("--no-recall", action="store_true", help="skip the attention-mass recall statistic")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="print a summary of a rocprofv3 --kernel-trace --stats output directory (no GPU needed)")
+    ap.add_argument("--summarize-pmc", metavar="DIR", nargs="+",
+                    help="print a summary of rocprofv3 --pmc output directories (no GPU needed)")
+    ap.add_argument("--timed-launches", type=int, default=0,
+                    help="with --summarize-trace: also average each kernel's last N launches (the timed region)")
     ap.add_argument("--fp8", action="store_true",
                     help="run the FP8 variant of the attention stage (ab_fp8_prepare + ab_attn_fwd_fp8: E4M3 "
                          "products, V-Smooth, ExpCast-FP8) instead of the bf16 kernel; not the headline line")
@@ -92,6 +103,35 @@ def read_traffic(workload, variant):
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+MFMA_BUSY = {
+    "bf16": (os.path.join(ROOT, "profiles", "attn_fwd_wan1.3b_mfma_busy.txt"),
+             os.path.join(ROOT, "block_sparse_attention_ibcs_amd", "csrc", "attn_fwd.hip")),
+    "fp8": (os.path.join(ROOT, "profiles", "attn_fp8_wan1.3b_mfma_busy.txt"),
+            os.path.join(ROOT, "block_sparse_attention_ibcs_amd", "csrc", "attn_fp8.hip")),
+}
+
+
+def read_mfma_busy(workload, variant):
+    """Fraction of the attention kernel's active cycles in which the matrix cores are busy
+    (SQ_VALU_MFMA_BUSY_CYCLES over SIMDs x GRBM_GUI_ACTIVE per XCD), from the committed
+    counter summary if it was taken on this workload with the current kernel source."""
+    summary, source = MFMA_BUSY[variant]
+    if not os.path.exists(summary):
+        return None
+    vals = {}
+    with open(summary) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                key, val = line.split(":", 1)
+                vals[key.strip()] = val.strip()
+    if vals.get("kernel_source_sha256_16") != source_digest(source) or vals.get("workload") != workload:
+        return None
+    try:
+        return float(vals["mfma_busy_fraction"])
     except (KeyError, ValueError):
         return None
 
@@ -364,9 +404,48 @@ def run_ablation(args):
         torch.cuda.empty_cache()
 
 
-def cpu_baseline(w, q, k, v, density, seed, budget_s):
+def mass_recall(w, q, k, scores, idx, wts, cnt, density, n_blocks=64, seed=5):
+    """Descriptive statistics of the synthetic inputs on n_blocks seeded query blocks:
+    the true attention mass of a query block on key sub-block j is the mean over its
+    rows of the dense softmax mass on j (float32 on the host). Reports the mass held by
+    the top-ceil(rho NKB) sub-blocks ranked by the true mass, and by the IBCS scores,
+    the mass on the sub-blocks the draw kept, and the draw's inverse-probability
+    weighted mass (whose expectation is 1)."""
+    import numpy as np
+
+    rng = np.random.default_rng(seed)
+    nqb = -(-w.N // w.q_block)
+    nkb = -(-w.N // w.k_block)
+    topk = min(nkb, math.ceil(density * nkb))
+    pick = rng.choice(w.B * w.H * nqb, size=min(n_blocks, w.B * w.H * nqb), replace=False)
+    scale = 1.0 / math.sqrt(w.d)
+    stats = {"true_topk": [], "ibcs_topk": [], "kept": [], "kept_weighted": []}
+    pad = nkb * w.k_block - w.N
+    for t in pick.tolist():
+        bh, i = divmod(t, nqb)
+        b, h = divmod(bh, w.H)
+        lo, hi = i * w.q_block, min(w.N, (i + 1) * w.q_block)
+        logit = (q[b, h, lo:hi].astype(np.float32) @ k[b, h].astype(np.float32).T) * np.float32(scale)
+        p = np.exp(logit - logit.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        if pad:
+            p = np.concatenate([p, np.zeros((p.shape[0], pad), np.float32)], axis=1)
+        mass = p.reshape(p.shape[0], nkb, w.k_block).sum(axis=2).mean(axis=0).astype(np.float64)
+        stats["true_topk"].append(np.sort(mass)[::-1][:topk].sum())
+        stats["ibcs_topk"].append(mass[np.argsort(-scores[b, h, i], kind="stable")[:topk]].sum())
+        c = int(cnt[b, h, i])
+        kept = idx[b, h, i, :c]
+        stats["kept"].append(mass[kept].sum())
+        stats["kept_weighted"].append((mass[kept] * wts[b, h, i, :c]).sum())
+    out = {key: float(np.mean(val)) for key, val in stats.items()}
+    out.update({"blocks": int(len(pick)), "top": int(topk)})
+    return out
+
+
+def cpu_baseline(w, q, k, v, density, seed, budget_s, precision="fp32"):
     """Time the oracle (IBCS + SIP + weighted attention) on query blocks for about budget_s seconds:
-    a seeded spread of the blocks of head 0, then of head 1, and so on."""
+    a seeded spread of the blocks of head 0, then of head 1, and so on. precision: the oracle's
+    fp32 timing mode (its score and attention arithmetic in float32) or its fp64 parity mode."""
     import numpy as np
 
     import oracle
@@ -385,7 +464,7 @@ def cpu_baseline(w, q, k, v, density, seed, budget_s):
     t0 = time.perf_counter()
     done = []
     for (b, h, i) in order:
-        oracle.run_blocks(q, k, v, p, seed, [(h // w.H, h % w.H, i)])
+        oracle.run_blocks(q, k, v, p, seed, [(h // w.H, h % w.H, i)], precision=precision)
         done.append(i)
         if time.perf_counter() - t0 >= budget_s and len(done) >= 2:
             break
@@ -398,15 +477,104 @@ def cpu_baseline(w, q, k, v, density, seed, budget_s):
         "unit": "TFLOP/s (dense-equivalent)",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"{len(done)} query blocks ({rows} query rows) of {heads} head(s) through IBCS k-means, block scores, "
-                  f"SIP draw and weighted attention in float64/numpy; {dt:.1f} s wall "
+        "sample": f"{len(done)} query blocks ({rows} query rows) of {heads} head(s) through IBCS k-means (fp32), "
+                  f"block scores, SIP draw (integer) and weighted attention, scores and attention in "
+                  f"{'float32' if precision == 'fp32' else 'float64'} numpy; {dt:.1f} s wall "
                   f"({dt / len(done) * w.H * w.nqb:.0f} s extrapolated per layer)",
+        "precision": precision,
         "ms_per_layer_extrapolated": dt / len(done) * w.H * w.nqb * 1e3,
     }
 
 
+def _csv_rows(path):
+    import csv
+
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def summarize_trace(args):
+    """Kernel-time table of a rocprofv3 --kernel-trace --stats run, plus each kernel's
+    average over its last --timed-launches launches (the timed region of a bench run)."""
+    import glob
+
+    stats = _csv_rows(glob.glob(os.path.join(args.summarize_trace, "*kernel_stats.csv"))[0])
+    print(f"# {'kernel':<32}{'calls':>6}{'avg_us':>10}{'min_us':>10}{'max_us':>10}{'share':>9}")
+    for r in stats:
+        print(f"{r['Name'][:32]:<32}{int(r['Calls']):>6}{float(r['AverageNs']) / 1e3:>10.1f}"
+              f"{float(r['MinNs']) / 1e3:>10.1f}{float(r['MaxNs']) / 1e3:>10.1f}{float(r['Percentage']):>8.2f}%")
+    if args.timed_launches > 0:
+        trace = _csv_rows(glob.glob(os.path.join(args.summarize_trace, "*kernel_trace.csv"))[0])
+        by = {}
+        for r in sorted(trace, key=lambda r: int(r["Start_Timestamp"])):
+            by.setdefault(r["Kernel_Name"], []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+        print(f"# last {args.timed_launches} launches of each kernel (timed region):")
+        for name, d in by.items():
+            if len(d) >= args.timed_launches:
+                last = d[-args.timed_launches:]
+                print(f"#   {name[:40]:<40} {sum(last) / len(last) / 1e3:10.1f} us")
+
+
+def summarize_pmc(args):
+    """Average per dispatch of every counter of rocprofv3 --pmc runs, per kernel; HBM
+    bytes of each kernel from FETCH_SIZE / WRITE_SIZE scaled by what the same counters
+    read for the device copy of known size (bench.py --copy-calibration-mib), and the
+    matrix-core busy fraction SQ_VALU_MFMA_BUSY_CYCLES / (SIMDs x GRBM_GUI_ACTIVE per XCD)."""
+    import glob
+
+    per = {}
+    agent = None
+    for d in args.summarize_pmc:
+        rows = _csv_rows(glob.glob(os.path.join(d, "*counter_collection.csv"))[0])
+        for r in rows:
+            key = (r["Kernel_Name"], r["Counter_Name"])
+            per.setdefault(key, {}).setdefault(r["Dispatch_Id"], 0.0)
+            per[key][r["Dispatch_Id"]] += float(r["Counter_Value"])
+        info = glob.glob(os.path.join(d, "*agent_info.csv"))
+        if info:
+            for a in _csv_rows(info[0]):
+                if a.get("Agent_Type") == "GPU":
+                    agent = a
+    avg = {key: sum(v.values()) / len(v) for key, v in per.items()}
+    kernels = sorted({k for k, _ in avg})
+    simds = int(agent["Simd_Count"]) if agent else 1024
+    xcds = int(agent["Num_Xcc"]) if agent else 8
+    for kname in kernels:
+        vals = {c: v for (k, c), v in avg.items() if k == kname}
+        print(f"{kname[:40]:<40} " + "  ".join(f"{c} {v:.6g}" for c, v in sorted(vals.items())))
+    copy = [k for k in kernels if "copyBuffer" in k]
+    mib = args.copy_calibration_mib
+    fetch_scale = write_scale = None
+    if copy and mib > 0:
+        # the calibration copy is the largest dispatch of the copy kernel (torch issues small ones too)
+        c = copy[0]
+        if (c, "FETCH_SIZE") in per:
+            fetch_scale = mib * 1024.0 / max(per[(c, "FETCH_SIZE")].values())
+        if (c, "WRITE_SIZE") in per:
+            write_scale = mib * 1024.0 / max(per[(c, "WRITE_SIZE")].values())
+        print(f"# calibration: a {mib} MiB device copy; fetch scale {fetch_scale}, write scale {write_scale} "
+              f"(true KiB per counted KiB)")
+    for kname in kernels:
+        out = []
+        if fetch_scale and (kname, "FETCH_SIZE") in avg:
+            out.append(f"fetch {avg[(kname, 'FETCH_SIZE')] * fetch_scale * 1024 / 1e6:.1f} MB")
+        if write_scale and (kname, "WRITE_SIZE") in avg:
+            out.append(f"write {avg[(kname, 'WRITE_SIZE')] * write_scale * 1024 / 1e6:.1f} MB")
+        if (kname, "SQ_VALU_MFMA_BUSY_CYCLES") in avg and (kname, "GRBM_GUI_ACTIVE") in avg:
+            busy = avg[(kname, "SQ_VALU_MFMA_BUSY_CYCLES")] / (simds * avg[(kname, "GRBM_GUI_ACTIVE")] / xcds)
+            out.append(f"mfma_busy {busy:.4f}")
+        if out:
+            print(f"# {kname[:40]:<40} " + ", ".join(out))
+
+
 def main():
     args = parse_args()
+    if args.summarize_trace or args.summarize_pmc:
+        if args.summarize_trace:
+            summarize_trace(args)
+        if args.summarize_pmc:
+            summarize_pmc(args)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path is single-GPU by design "
               "(on several GPUs the heads would be split between them, each GPU running the whole path "
@@ -532,8 +700,28 @@ def main():
     torch.cuda.synchronize()
     stage_ms = {k_: float(np.mean([a.elapsed_time(b) for a, b in v_])) for k_, v_ in ev.items()}
 
+    # cold caches: a 512 MB buffer (twice the 256 MB Infinity Cache, far beyond the L2s)
+    # written before each timed step, outside its events
+    cold = None
+    if args.cold_steps > 0:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        cold_ev = {name: [] for name in ev}
+        for n_c in range(args.cold_steps):
+            flush.fill_(n_c & 0xFF)
+            saved = {name: len(v_) for name, v_ in ev.items()}
+            step(record=True)
+            for name in ev:
+                cold_ev[name].extend(ev[name][saved[name]:])
+                del ev[name][saved[name]:]
+        torch.cuda.synchronize()
+        cold_stage = {k_: float(np.mean([a.elapsed_time(b) for a, b in v_])) for k_, v_ in cold_ev.items()}
+        cold = {"steps": args.cold_steps, "stage_ms": cold_stage, "ms_per_step": float(sum(cold_stage.values())),
+                "flush": "512 MB buffer written before each step (outside the timed events)"}
+        del flush
+
     actual_flops, realised = attention_work(w, nqb, nkb, idx, cnt)
     dense = w.dense_flops()
+    K_budget = max(1, min(nkb, math.floor(density * nkb + 0.5)))
 
     attn_s = stage_ms["attn"] / 1e3
     achieved = actual_flops / attn_s / 1e12
@@ -567,7 +755,11 @@ def main():
             "heads": w.H,
             "density": density,
             "realised_density": realised,
+            # sum of the inclusion probabilities of a row is the budget K (up to integer
+            # floors below NKB 2^-24), so the expected kept fraction is K / NKB
+            "expected_density": K_budget / nkb,
             "stage_ms": stage_ms,
+            "cold_cache": cold,
             "hip_graph": bool(args.graph),
             "attention_variant": "bf16" if fp8_ops is None else "fp8 (E4M3 QK and PV, V-Smooth, ExpCast-FP8)",
             "fp8_rel_l2_vs_bf16_path": fp8_vs_bf16,
@@ -583,13 +775,19 @@ def main():
             "unit": "TFLOP/s",
             "frac": achieved / peak,
             "traffic": traffic,
+            "traffic_note": "FETCH_SIZE + WRITE_SIZE per launch scaled by a device-copy calibration: bytes between "
+                            "L2 and the fabric (Infinity Cache hits included), an upper bound on HBM bytes",
+            "mfma_busy": read_mfma_busy(args.workload, "bf16" if fp8_ops is None else "fp8"),
             "flops_per_launch": actual_flops,
             "launch_ms": stage_ms["attn"],
         },
         "cpu_baseline": None,
     }
+    if not args.no_recall:
+        result["config"]["attention_mass_recall"] = mass_recall(
+            w, q, k, scores.cpu().numpy(), idx.cpu().numpy(), wts.cpu().numpy(), cnt.cpu().numpy(), density)
     if not args.no_cpu_baseline and fp8_ops is None:
-        result["cpu_baseline"] = cpu_baseline(w, q, k, v, density, args.seed, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(w, q, k, v, density, args.seed, args.cpu_seconds, args.cpu_precision)
     print(json.dumps(result), flush=True)
 
 

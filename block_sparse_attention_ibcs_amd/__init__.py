@@ -139,11 +139,13 @@ _lib = None
 
 
 def load_library():
-    """Load libabattn.so from this package (built by block_sparse_attention_ibcs_amd.build)."""
+    """Load libabattn.so from this package (built by block_sparse_attention_ibcs_amd.build);
+    the environment variable AB_ATTN_LIBRARY names another build of it (e.g. one with the
+    host code compiled under sanitizers)."""
     global _lib
     if _lib is not None:
         return _lib
-    path = library_path()
+    path = os.environ.get("AB_ATTN_LIBRARY") or library_path()
     if not os.path.exists(path):
         raise ImportError(f"{path} is missing: build it with `python -m block_sparse_attention_ibcs_amd.build`")
     lib = ctypes.CDLL(path)

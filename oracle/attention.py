@@ -30,29 +30,30 @@ def dense_attention(q, k, v, scale):
     return out, lse
 
 
-def sparse_ht_attention(q, k, v, idx, weight, k_block, scale):
+def sparse_ht_attention(q, k, v, idx, weight, k_block, scale, dtype=np.float64):
     """Weighted attention of one query block over its kept key sub-blocks.
 
     q [n, d]; k, v [N, d] of the same (b, h); idx: kept sub-block indices;
-    weight: omega_j per kept sub-block. Returns (O [n, d], LSE [n]) in float64.
+    weight: omega_j per kept sub-block. Returns (O [n, d], LSE [n]) in float64
+    (dtype=np.float32: the same steps in float32, the CPU timing mode).
     """
-    q = np.asarray(q, dtype=np.float64)
+    q = np.asarray(q, dtype=dtype)
     n, d = q.shape
     idx = np.asarray(idx, dtype=np.int64)
     if idx.size == 0:
-        return np.zeros((n, d)), np.full(n, -np.inf)
-    k = np.asarray(k, dtype=np.float64)
-    v = np.asarray(v, dtype=np.float64)
+        return np.zeros((n, d), dtype), np.full(n, -np.inf, dtype)
+    k = np.asarray(k, dtype=dtype)
+    v = np.asarray(v, dtype=dtype)
     N = k.shape[0]
     keys = []
     omega = []
-    for j, w in zip(idx.tolist(), np.asarray(weight, dtype=np.float64).tolist()):
+    for j, w in zip(idx.tolist(), np.asarray(weight, dtype=dtype).tolist()):
         lo, hi = j * k_block, min(N, (j + 1) * k_block)
         keys.append(np.arange(lo, hi))
         omega.append(np.full(hi - lo, w))
     keys = np.concatenate(keys)
-    omega = np.concatenate(omega)
-    s = float(scale) * (q @ k[keys].T)  # [n, kept keys]
+    omega = np.concatenate(omega).astype(dtype)
+    s = dtype(scale) * (q @ k[keys].T)  # [n, kept keys]
     m = s.max(axis=1, keepdims=True)
     a = np.exp(s - m) * omega[None, :]
     den = a.sum(axis=1, keepdims=True)

@@ -168,29 +168,30 @@ def _logsumexp(x, axis):
     return np.squeeze(m, axis=axis) + np.log(np.sum(np.exp(x - m), axis=axis))
 
 
-def block_scores(mu, sizes, n_rows, K, k_block, scale, bf16):
-    """Block-importance estimates of one query block, float64 math, fp32 result.
+def block_scores(mu, sizes, n_rows, K, k_block, scale, bf16, dtype=np.float64):
+    """Block-importance estimates of one query block, float64 math, fp32 result
+    (dtype=np.float32: the same steps in float32, the CPU timing mode).
 
     mu: float32 [C, d] centroids; sizes: [C] member counts; n_rows: rows in the
     query block; K: [N, d] keys (the exact values the GPU sees); k_block: Bk.
     Returns float32 [NKB].
     """
     mu = np.asarray(mu, dtype=np.float32)
-    K = np.asarray(K, dtype=np.float64)
+    K = np.asarray(K, dtype=dtype)
     N = K.shape[0]
     nkb = -(-N // k_block)
     if bf16:
         c2 = np.float32(np.float32(scale) * np.float32(np.log2(np.e)))
         mu2 = round_bf16((mu * c2).astype(np.float32))  # scale * log2(e) * mu at bf16
-        logits = np.log(2.0) * (mu2.astype(np.float64) @ K.T)  # base-2 logits in natural units
+        logits = dtype(np.log(2.0)) * (mu2.astype(dtype) @ K.T)  # base-2 logits in natural units
     else:
-        logits = float(scale) * (mu.astype(np.float64) @ K.T)  # [C, N]
+        logits = dtype(scale) * (mu.astype(dtype) @ K.T)  # [C, N]
     pad = nkb * k_block - N
     if pad:
         logits = np.concatenate([logits, np.full((logits.shape[0], pad), -np.inf)], axis=1)
     ell = _logsumexp(logits.reshape(logits.shape[0], nkb, k_block), axis=2)  # [C, NKB]
     L = _logsumexp(ell, axis=1)  # [C]
-    w = np.asarray(sizes, dtype=np.float64) / float(n_rows)
+    w = np.asarray(sizes, dtype=dtype) / dtype(n_rows)
     s = (w[:, None] * np.exp(ell - L[:, None])).sum(axis=0)
     return s.astype(np.float32)
 

@@ -30,14 +30,17 @@ class Params:
         return self.scale if self.scale > 0 else 1.0 / math.sqrt(d)
 
 
-def run_blocks(q, k, v, p, seed, blocks, with_attention=True):
+def run_blocks(q, k, v, p, seed, blocks, with_attention=True, precision="fp64"):
     """Run the path on query blocks `blocks` = [(b, h, i), ...].
 
     q, k, v: float32 [B, H, N, d] holding exactly the values the GPU sees.
     Returns a dict keyed by (b, h, i) with centroids/sizes/assign, the fp32
     score row, the SIP draw (count/idx/weight/thresh/mask) and, when asked,
     O (float64 [n_i, d]) and LSE (float64 [n_i]).
+    precision: "fp64" (parity) or "fp32" (the same steps with the score and
+    attention arithmetic in float32: the CPU timing mode).
     """
+    dt = np.float64 if precision == "fp64" else np.float32
     B, H, N, d = q.shape
     scale = p.softmax_scale(d)
     nkb = -(-N // p.k_block)
@@ -47,7 +50,7 @@ def run_blocks(q, k, v, p, seed, blocks, with_attention=True):
     for (b, h, i) in blocks:
         lo, hi = i * p.q_block, min(N, (i + 1) * p.q_block)
         mu, sizes, assign = kmeans_fp32(q[b, h, lo:hi], p.n_clusters, p.kmeans_iters)
-        s = block_scores(mu, sizes, hi - lo, k[b, h], p.k_block, scale, p.bf16)
+        s = block_scores(mu, sizes, hi - lo, k[b, h], p.k_block, scale, p.bf16, dtype=dt)
         res[(b, h, i)] = {"mu": mu, "sizes": sizes, "assign": assign, "scores": s}
         scores[(b, h, i)] = s
 
@@ -63,7 +66,8 @@ def run_blocks(q, k, v, p, seed, blocks, with_attention=True):
         if with_attention:
             b, h, i = key
             lo, hi = i * p.q_block, min(N, (i + 1) * p.q_block)
-            o, lse = sparse_ht_attention(q[b, h, lo:hi], k[b, h], v[b, h], dr["idx"], dr["weight"], p.k_block, scale)
+            o, lse = sparse_ht_attention(q[b, h, lo:hi], k[b, h], v[b, h], dr["idx"], dr["weight"], p.k_block, scale,
+                                         dtype=dt)
             res[key]["O"] = o
             res[key]["LSE"] = lse
     return res

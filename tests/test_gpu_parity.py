@@ -785,6 +785,35 @@ def test_empty_rows_give_zero_output():
     np.testing.assert_array_equal(out[0, 0, :64], run.out[0, 0, :64])
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_counts_outside_the_row_are_clamped(dtype):
+    """A count above NKB on a row that is not the last one is clamped to NKB (the
+    kernels read no list entry or weight past the row), and a negative count acts as 0:
+    the outputs equal those of the same lists with the counts NKB and 0."""
+    dev = _gpu()
+    N, H, d, Bq, Bk = 1000, 1, 128, 128, 32
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    g = torch.Generator().manual_seed(8)
+    q, k, v = (torch.randn((1, H, N, d), generator=g).to(tdt).to(dev) for _ in range(3))
+    desc = ab.Desc.for_tensor(q, Bq, Bk, 8)
+    nqb, nkb = desc.nqb, desc.nkb
+    idx = torch.arange(nkb, dtype=torch.int32, device=dev).repeat(1, H, nqb, 1).contiguous()
+    wts = torch.ones((1, H, nqb, nkb), dtype=torch.float32, device=dev)
+    cnt = torch.full((1, H, nqb), nkb, dtype=torch.int32, device=dev)
+    ref_out, ref_lse = ab.ab_attn_fwd(desc, q, k, v, idx, wts, cnt)
+    cnt_bad = cnt.clone()
+    cnt_bad[0, 0, 2] = nkb + 1000  # not the last row: its list is followed by other rows'
+    cnt_bad[0, 0, 4] = -5
+    out, lse = ab.ab_attn_fwd(desc, q, k, v, idx, wts, cnt_bad)
+    torch.cuda.synchronize()
+    rows = lambda i: slice(i * Bq, min(N, (i + 1) * Bq))  # noqa: E731
+    assert torch.equal(out[0, 0, rows(2)], ref_out[0, 0, rows(2)])
+    assert torch.equal(lse[0, 0, rows(2)], ref_lse[0, 0, rows(2)])
+    assert torch.all(out[0, 0, rows(4)] == 0) and torch.all(torch.isneginf(lse[0, 0, rows(4)]))
+    for i in (0, 1, 3, 5, 6, 7):
+        assert torch.equal(out[0, 0, rows(i)], ref_out[0, 0, rows(i)]), i
+
+
 def test_injected_index_lists_bf16():
     """Attention on hand-made lists: unsorted-free ascending lists with the ragged tail block and weights != 1."""
     _gpu()
