@@ -572,6 +572,55 @@ def test_fp32_shapes(N, H, d, Bq, Bk, C, T, density):
             assert np.abs(run.lse[0, h] - lse).max() <= 1e-5
 
 
+BATCHED = [
+    # (B, N, H, d, Bq, Bk, C, T, density, dtype): more than one batch entry
+    (2, 700, 2, 128, 128, 32, 8, 4, 0.3, "bf16"),
+    (3, 520, 1, 64, 64, 16, 4, 2, 0.4, "bf16"),
+    (2, 300, 2, 128, 128, 64, 8, 3, 0.5, "fp32"),
+]
+
+
+@pytest.mark.parametrize("B,N,H,d,Bq,Bk,C,T,density,dtype", BATCHED)
+def test_batched_shapes(B, N, H, d, Bq, Bk, C, T, density, dtype):
+    """B > 1: every query block of every batch entry through k-means, scores, the draw
+    (whose Philox counter carries b) and attention against the oracle; and the batch
+    entries are independent: k-means of entry b equals a B = 1 run on entry b's inputs
+    bit for bit, and so does attention on entry b's kept lists."""
+    _gpu()
+    w = workloads.Workload("batched", B, H, (1, 1, N), d, dtype, Bq, Bk, C, density, 0.5, False, kmeans_iters=T)
+    rng = np.random.default_rng(B * 1000 + N + d)
+    base = rng.standard_normal((B, H, N, d)).astype(np.float32)
+    q = (base + 0.5 * rng.standard_normal((B, H, N, d))).astype(np.float32)
+    k = (base + 0.5 * rng.standard_normal((B, H, N, d))).astype(np.float32)
+    v = rng.standard_normal((B, H, N, d)).astype(np.float32)
+    if dtype == "bf16":
+        q, k, v = (workloads.round_to_bf16(x) for x in (q, k, v))
+    run = Run(w, inputs=(q, k, v), seed=11)
+    blocks = run.blocks(10**6)
+    assert len(blocks) == B * H * w.nqb
+    check_kmeans(run, blocks)
+    check_scores(run, blocks)
+    check_sampler(run, blocks)
+    check_sampler_every_row(run.scores, run.density, run.seed, run.idx, run.wts, run.cnt, run.mask, tag="batched")
+    check_attention(run, blocks)
+    dbg = ab.ab_score_debug(run.desc, run.qd)
+    torch.cuda.synchronize()
+    cent, sizes, assign = (x.cpu().numpy() for x in dbg)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    for b in range(B):
+        qd, kd, vd = (_to_dev(np.ascontiguousarray(x[b:b + 1]), tdt) for x in (q, k, v))
+        desc = ab.Desc.for_tensor(qd, Bq, Bk, C, T)
+        dbg1 = ab.ab_score_debug(desc, qd)
+        torch.cuda.synchronize()
+        c1, s1, a1 = (x.cpu().numpy() for x in dbg1)
+        assert np.array_equal(c1[0].view(np.uint32), cent[b].view(np.uint32)), b
+        assert np.array_equal(s1[0], sizes[b]) and np.array_equal(a1[0], assign[b]), b
+        out1, lse1 = ab.ab_attn_fwd(desc, qd, kd, vd, run.idx_d[b:b + 1].contiguous(), run.wts_d[b:b + 1].contiguous(),
+                                    run.cnt_d[b:b + 1].contiguous())
+        torch.cuda.synchronize()
+        assert torch.equal(out1[0], run.out_d[b]) and torch.equal(lse1[0], run.lse_d[b]), b
+
+
 def _reference_path_inputs():
     """Q, K, V (bf16 values, [1, 1, 1024, 128]) whose centroid logits reach every
     branch of the scorer's running reference: query blocks 0, 2, 4, 5, 7 stay within
