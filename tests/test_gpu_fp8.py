@@ -190,6 +190,13 @@ def test_attn_fp8_dense_and_peaked():
     _check_attn(q, k, v, 32, 1.0, seed=7)
 
 
+def test_attn_fp8_two_batch_entries():
+    """B = 2 (and a ragged N): every query block of both entries against the oracle,
+    with an empty row in the second entry."""
+    q, k, v = _bf16_inputs((2, 2, 260, 128), seed=31, offset=1.0)
+    _check_attn(q, k, v, 32, 0.4, seed=31, empty_row=(1, 0, 1))
+
+
 def test_attn_fp8_extreme_logits():
     """Query blocks whose logits reach +-200 in base-2 units, lie below -40 everywhere,
     or jump by more than 64 within a row's list (the inputs of the scorer's

@@ -1029,6 +1029,24 @@ def test_intra_patterns(N, H, d, Bq, Bk, L, layer):
 
 
 @pytest.mark.parametrize("layer", [0, 1])
+def test_intra_two_batch_entries(layer):
+    """INTRA lists and the attention over them with B = 2: the static lists repeat for
+    every (b, h), the processing order covers both entries, and every query block of
+    both entries matches the oracle."""
+    N, H, d, Bq, Bk, L = 700, 2, 128, 128, 32, 256
+    w = workloads.Workload("intra", 2, H, (1, 1, N), d, "bf16", Bq, Bk, 8, 0.1, 0.5, False)
+    rng = np.random.default_rng(4242 + layer)
+    base = rng.standard_normal((2, H, N, d)).astype(np.float32)
+    inputs = tuple(workloads.round_to_bf16(x) for x in (
+        base + 0.5 * rng.standard_normal((2, H, N, d)).astype(np.float32),
+        base + 0.5 * rng.standard_normal((2, H, N, d)).astype(np.float32),
+        rng.standard_normal((2, H, N, d)).astype(np.float32)))
+    run = _IntraRun(w, inputs, layer, L)
+    _check_intra_lists(run, layer, L)
+    check_attention(run, [(b, h, i) for b in range(2) for h in range(H) for i in range(w.nqb)])
+
+
+@pytest.mark.parametrize("layer", [0, 1])
 @pytest.mark.parametrize("name", ["wan1.3b", "hunyuan"])
 def test_intra_video_shape(name, layer):
     """Video shapes with the default neighbourhood (a partial last one in both): the

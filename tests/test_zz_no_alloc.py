@@ -31,6 +31,9 @@ def test_noalloc_matches_ab_score_on_two_calls():
     cases = [
         # the 40-head, 75600-token shape: one head needs ~49 MB, so several chunks of heads
         (1, 40, 75600, 128, torch.bfloat16, 128, 32, 8),
+        # smaller: two batch entries of six heads; chunks of three heads, so two chunk
+        # boundaries fall inside a batch entry
+        (2, 6, 75600, 128, torch.bfloat16, 128, 32, 8),
         # then a smaller, ragged problem in one chunk
         (2, 3, 5001, 64, torch.bfloat16, 64, 16, 4),
     ]
