@@ -130,11 +130,11 @@ def _lists(B, H, nqb, nkb, density, seed, empty_row=None):
     return idx, w, cnt
 
 
-def _check_attn(q, k, v, bk, density, seed, blocks=None, rows_per_block=None, empty_row=None):
+def _check_attn(q, k, v, bk, density, seed, blocks=None, rows_per_block=None, empty_row=None, scale=0.0):
     dev = _gpu()
     bq = 128
     qd, kd, vd = (x.to(dev) for x in (q, k, v))
-    desc = ab.Desc.for_tensor(qd, bq, bk, 1)
+    desc = ab.Desc.for_tensor(qd, bq, bk, 1, scale=scale)
     B, H, N, d = q.shape
     idx, w, cnt = _lists(B, H, desc.nqb, desc.nkb, density, seed, empty_row)
     ops = ab.ab_fp8_prepare(desc, qd, kd, vd)
@@ -155,7 +155,7 @@ def _check_attn(q, k, v, bk, density, seed, blocks=None, rows_per_block=None, em
             if rows_per_block is not None:
                 rows = sorted(set([r0, r1 - 1] + list(rng.choice(rows, min(rows_per_block, len(rows)), replace=False))))
             res = fp8.attn_rows_fp8(prep, idx[b:b + 1, h:h + 1], w[b:b + 1, h:h + 1], cnt[b:b + 1, h:h + 1],
-                                    bq, bk, desc_scale(d), [(0, 0, r) for r in rows])
+                                    bq, bk, scale if scale > 0 else desc_scale(d), [(0, 0, r) for r in rows])
             o_ref = np.stack([res[(0, 0, r)][0] for r in rows])
             l_ref = np.array([res[(0, 0, r)][1] for r in rows])
             got = out[b, h, rows]
@@ -188,6 +188,12 @@ def test_attn_fp8_dense_and_peaked():
     k = torch.randn((1, 1, 256, 128), generator=g).to(torch.bfloat16)
     v = (torch.randn((1, 1, 256, 128), generator=g) + 4).to(torch.bfloat16)
     _check_attn(q, k, v, 32, 1.0, seed=7)
+
+
+def test_attn_fp8_explicit_scale():
+    """A caller-given softmax scale (0.2 instead of 1/sqrt(128)) in the FP8 kernel."""
+    q, k, v = _bf16_inputs((1, 2, 300, 128), seed=77, offset=1.0)
+    _check_attn(q, k, v, 32, 0.4, seed=77, scale=0.2)
 
 
 def test_attn_fp8_two_batch_entries():

@@ -56,7 +56,7 @@ def _to_dev(x, dtype):
 class Run:
     """Inputs of one workload on host and device, and the GPU outputs of the whole path."""
 
-    def __init__(self, w, density=None, seed=0, data_seed=0, inputs=None):
+    def __init__(self, w, density=None, seed=0, data_seed=0, inputs=None, scale=0.0):
         _gpu()
         self.w = w
         self.density = w.density if density is None else density
@@ -64,9 +64,11 @@ class Run:
         self.q, self.k, self.v = inputs if inputs is not None else workloads.generate(w, seed=data_seed)
         tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
         self.qd, self.kd, self.vd = (_to_dev(x, tdt) for x in (self.q, self.k, self.v))
-        self.desc = ab.Desc.for_tensor(self.qd, w.q_block, w.k_block, w.n_clusters, w.kmeans_iters)
-        self.params = Params(w.q_block, w.k_block, w.n_clusters, w.kmeans_iters, self.density, bf16=w.dtype == "bf16")
-        self.scale = 1.0 / math.sqrt(w.d)
+        self.desc = ab.Desc.for_tensor(self.qd, w.q_block, w.k_block, w.n_clusters, w.kmeans_iters, scale=scale)
+        self.params = Params(w.q_block, w.k_block, w.n_clusters, w.kmeans_iters, self.density, bf16=w.dtype == "bf16",
+                             scale=scale)
+        # the softmax scale: the caller's when positive, else 1/sqrt(d)
+        self.scale = self.params.softmax_scale(w.d)
         self.run_gpu()
 
     def run_gpu(self):
@@ -570,6 +572,30 @@ def test_fp32_shapes(N, H, d, Bq, Bk, C, T, density):
             o, lse = dense_attention(q[0, h], k[0, h], v[0, h], run.scale)
             assert np.abs(run.out[0, h] - o).max() <= 1e-5
             assert np.abs(run.lse[0, h] - lse).max() <= 1e-5
+
+
+@pytest.mark.parametrize("scale,dtype", [(0.05, "bf16"), (0.3, "bf16"), (0.3, "fp32")])
+def test_explicit_softmax_scale(scale, dtype):
+    """A caller-given softmax scale instead of 1/sqrt(d): the scorer's base-2 centroid
+    operand, the scores, the draw and attention all follow it (every query block against
+    the oracle at the same scale)."""
+    _gpu()
+    N, H, d = 700, 2, 128
+    w = workloads.Workload("scale", 1, H, (1, 1, N), d, dtype, 128, 32, 8, 0.3, 0.5, False, kmeans_iters=3)
+    rng = np.random.default_rng(int(scale * 1000))
+    base = rng.standard_normal((1, H, N, d)).astype(np.float32)
+    q = (base + 0.5 * rng.standard_normal((1, H, N, d))).astype(np.float32)
+    k = (base + 0.5 * rng.standard_normal((1, H, N, d))).astype(np.float32)
+    v = rng.standard_normal((1, H, N, d)).astype(np.float32)
+    if dtype == "bf16":
+        q, k, v = (workloads.round_to_bf16(x) for x in (q, k, v))
+    run = Run(w, inputs=(q, k, v), seed=4, scale=scale)
+    assert run.scale == scale
+    blocks = run.blocks(10**6)
+    check_kmeans(run, blocks)
+    check_scores(run, blocks)
+    check_sampler(run, blocks)
+    check_attention(run, blocks)
 
 
 BATCHED = [
