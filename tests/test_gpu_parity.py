@@ -509,6 +509,9 @@ EDGE = [
     (1000, 2, 128, 128, 32, 8, 4, 1.0),
     (130, 1, 128, 128, 128, 8, 4, 0.01),
     (70, 1, 64, 64, 16, 4, 4, 1.0),
+    (1, 1, 128, 128, 32, 8, 4, 0.5),  # one token: one row, one cluster, one sub-block
+    (17, 2, 64, 64, 32, 4, 3, 1.0),  # fewer tokens than one key sub-block
+    (1000, 2, 128, 128, 32, 16, 16, 0.3),  # 16 clusters (their own assembly kernel), 16 iterations
 ]
 
 
@@ -544,6 +547,7 @@ FP32_SHAPES = [
     (200, 1, 128, 128, 128, 8, 4, 1.0),
     (190, 1, 64, 64, 16, 64, 2, 0.25),
     (333, 1, 128, 128, 16, 128, 1, 0.2),
+    (400, 1, 64, 64, 16, 16, 8, 0.3),
 ]
 
 
