@@ -12,7 +12,8 @@
 // densely.
 //
 // bf16 design (gfx950, wave64): one workgroup per (b, h, query block); each
-// wave owns 32 query rows. A tile is 64 key slots: the compacted list of kept
+// wave owns 32 query rows (at q_block 64 and d 128, two waves per 32 rows, each
+// with one 32-slot half of every tile, merged at the end). A tile is 64 key slots: the compacted list of kept
 // sub-blocks is laid end to end, so a 64-slot tile holds 64/Bk sub-blocks for
 // Bk <= 64 and half of one for Bk = 128; the gather is one coalesced run per
 // sub-block row into LDS. The logits are computed transposed,
@@ -36,7 +37,13 @@ constexpr int kSlots = 64;
 
 template <int D, int BQ, int BK>
 struct AttnCfg {
-  static constexpr int kWaves = BQ / 32;           // each wave owns 32 query rows
+  // Bq = 64 at d = 128: four waves, two per 32 query rows, each taking one 32-slot half
+  // of every tile, so a CU still holds two workgroups of four waves (64 KB of LDS each;
+  // with two waves per workgroup it would hold one wave per SIMD); the two softmax
+  // states of a row are merged at the end.
+  static constexpr bool kSplit = BQ == 64 && D == 128;
+  static constexpr int kWaves = kSplit ? 4 : BQ / 32;  // each wave owns 32 query rows
+  static constexpr int kHalves = kSplit ? 1 : 2;       // 32-slot halves of a tile per wave
   static constexpr int kThreads = kWaves * 64;
   static constexpr int kRowBytes = D * 2;          // one key row of K or V
   static constexpr int kChunks = D / 8;            // 16-byte chunks per row
@@ -71,7 +78,7 @@ __device__ __forceinline__ constexpr int slot_entry(int s) {
 }
 
 template <int D, int BQ, int BK>
-__global__ __launch_bounds__(BQ * 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__((AttnCfg<D, BQ, BK>::kThreads)) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_bf16(Dims P, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                    const uint16_t* __restrict__ v, const int32_t* __restrict__ idx,
                    const float* __restrict__ weights, const int32_t* __restrict__ counts,
@@ -88,6 +95,9 @@ void attn_fwd_bf16(Dims P, const uint16_t* __restrict__ q, const uint16_t* __res
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, col = lane & 31;
+  constexpr int HB = Cfg::kHalves;
+  const int qsel = Cfg::kSplit ? (wave & 1) : wave;  // this wave's 32 query rows
+  const int sh = Cfg::kSplit ? (wave >> 1) : 0;      // its 32-slot half of each tile (split)
   int blk = xcd_remap(blockIdx.x, gridDim.x);  // (b*H + h)*nqb + i
   if (order) {  // the caller's processing order; rows outside the grid are skipped
     blk = order[blk];
@@ -109,7 +119,7 @@ void attn_fwd_bf16(Dims P, const uint16_t* __restrict__ q, const uint16_t* __res
       __builtin_amdgcn_make_buffer_rsrc((void*)(v + size_t(bh) * N * D), (short)0, head_bytes, 0x00020000);
 
   // Q^T as the B operand: lane -> query row (wave*32 + col), 8 dims per k step
-  const int qr = wave * 32 + col;
+  const int qr = qsel * 32 + col;
   bf16x8_t qf[D / 16];
   {
     const uint16_t* src = q + (size_t(bh) * N + row0 + min(qr, n - 1)) * D + half * 8;
@@ -188,13 +198,19 @@ void attn_fwd_bf16(Dims P, const uint16_t* __restrict__ q, const uint16_t* __res
 #pragma unroll
     for (int e = 0; e < Cfg::kTileEntries; ++e) le[e] = __builtin_amdgcn_logf(wv[e]);
 #pragma unroll
-    for (int g = 0; g < 8; ++g) lwg[g] = le[slot_entry<BK>((g >> 2) * 32 + (g & 3) * 8)];
+    for (int g = 0; g < 4 * HB; ++g) {
+      if constexpr (Cfg::kSplit)
+        lwg[g] = sh ? le[slot_entry<BK>(32 + (g & 3) * 8)] : le[slot_entry<BK>((g & 3) * 8)];
+      else
+        lwg[g] = le[slot_entry<BK>((g >> 2) * 32 + (g & 3) * 8)];
+    }
   };
 
   // LDS byte offsets of this lane's fragment reads (independent of the tile)
   int koff[D / 16];  // K rows col (+32 for the second half), chunk 2*kk + half
 #pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) koff[kk] = col * Cfg::kRowBytes + (((2 * kk + half) ^ k_swz<D>(col)) << 4);
+  for (int kk = 0; kk < D / 16; ++kk)
+    koff[kk] = (sh * 32 + col) * Cfg::kRowBytes + (((2 * kk + half) ^ k_swz<D>(col)) << 4);
   // transposed V read: lane J of 16-lane group G points at slot (J%16)/4 of its group's
   // 4-slot run and dims 4*((J%16)%4) of its 16-dim half of each 32-dim block
   const int tgrp = lane >> 4, tj = lane & 15;
@@ -203,7 +219,7 @@ void attn_fwd_bf16(Dims P, const uint16_t* __restrict__ q, const uint16_t* __res
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) {
     const int byte = db * 64 + (tgrp & 1) * 32 + (tj & 3) * 8;  // logical byte within the row
-    voff[db] = tr_slot * Cfg::kRowBytes + ((((byte >> 4) ^ v_swz<D>(tr_slot)) << 4) | (byte & 15));
+    voff[db] = (sh * 32 + tr_slot) * Cfg::kRowBytes + ((((byte >> 4) ^ v_swz<D>(tr_slot)) << 4) | (byte & 15));
   }
 
   int kv[Cfg::kWaveEntries];
@@ -228,29 +244,31 @@ void attn_fwd_bf16(Dims P, const uint16_t* __restrict__ q, const uint16_t* __res
     if (t + 1 < ntiles) issue_tile(t + 1, kn, vn, kv);  // lands while tile t is computed
     if (t + 2 < ntiles) entries(t + 2, kv);
     if (t + 1 < ntiles) tile_weights(t + 1, wv);
-    // S^T for both 32-slot halves, as two independent accumulation chains
-    f32x16_t acc[2];
+    // (split) a wave whose half of the tile holds only padding has nothing to add
+    if (Cfg::kSplit && t * kSlots + sh * 32 >= vend) return;
+    // S^T for this wave's 32-slot halves, as independent accumulation chains
+    f32x16_t acc[HB];
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) acc[hb] = f32x16_t{};
+    for (int hb = 0; hb < HB; ++hb) acc[hb] = f32x16_t{};
     // The K fragments of step kk + 1 are read before the products of step kk are
     // issued, so each read has two products' time to land (the scheduling-group
     // barriers keep the compiler from sinking the reads next to their use).
     {
-      uint4 kf[2][2];
+      uint4 kf[2][HB];
 #pragma unroll
-      for (int hb = 0; hb < 2; ++hb) kf[0][hb] = *reinterpret_cast<const uint4*>(kc + hb * 32 * Cfg::kRowBytes + koff[0]);
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+      for (int hb = 0; hb < HB; ++hb) kf[0][hb] = *reinterpret_cast<const uint4*>(kc + hb * 32 * Cfg::kRowBytes + koff[0]);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, HB, 0);
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
         if (kk + 1 < D / 16) {
 #pragma unroll
-          for (int hb = 0; hb < 2; ++hb)
+          for (int hb = 0; hb < HB; ++hb)
             kf[(kk + 1) & 1][hb] = *reinterpret_cast<const uint4*>(kc + hb * 32 * Cfg::kRowBytes + koff[kk + 1]);
-          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, HB, 0);
         }
 #pragma unroll
-        for (int hb = 0; hb < 2; ++hb) acc[hb] = mfma32x32x16(as_bf16x8(kf[kk & 1][hb]), qf[kk], acc[hb]);
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
+        for (int hb = 0; hb < HB; ++hb) acc[hb] = mfma32x32x16(as_bf16x8(kf[kk & 1][hb]), qf[kk], acc[hb]);
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, HB, 0);
       }
     }
     // The V operands of the first D/32 products of O^T += V^T P^T are read now, so
@@ -271,10 +289,10 @@ void attn_fwd_bf16(Dims P, const uint16_t* __restrict__ q, const uint16_t* __res
     const bool ragged = (t + 1) * kSlots > vend;
     if (ragged) {
 #pragma unroll
-      for (int hb = 0; hb < 2; ++hb)
+      for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int gs = t * kSlots + hb * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
+          const int gs = t * kSlots + (sh + hb) * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
           if (gs >= vend) acc[hb][e] = -__builtin_inff();
         }
     }
@@ -286,11 +304,11 @@ void attn_fwd_bf16(Dims P, const uint16_t* __restrict__ q, const uint16_t* __res
     // O and l far from overflow.
     // The row sum adds the bf16-rounded probabilities, two per dot2 instruction:
     // the same values the P V product uses.
-    bf16x8_t pb[4];
+    bf16x8_t pb[2 * HB];
     float ps;
     auto probs = [&]() {
 #pragma unroll
-      for (int g = 0; g < 8; ++g) {
+      for (int g = 0; g < 4 * HB; ++g) {
         const float bias = lwg[g] - m;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
@@ -299,7 +317,7 @@ void attn_fwd_bf16(Dims P, const uint16_t* __restrict__ q, const uint16_t* __res
       const bf16x2_t ones = {__bf16(1.0f), __bf16(1.0f)};
       float s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < 2 * HB; ++j) {
         s0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2_t{pb[j][0], pb[j][1]}, ones, s0, false);
         s1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2_t{pb[j][2], pb[j][3]}, ones, s1, false);
         s0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2_t{pb[j][4], pb[j][5]}, ones, s0, false);
@@ -313,11 +331,14 @@ void attn_fwd_bf16(Dims P, const uint16_t* __restrict__ q, const uint16_t* __res
 #pragma unroll
       for (int e = 1; e < 16; ++e) amax = fmaxf(amax, acc[0][e]);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) amax = fmaxf(amax, acc[1][e]);
+      for (int hb = 1; hb < HB; ++hb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) amax = fmaxf(amax, acc[hb][e]);
       float lwmax = lwg[0];
 #pragma unroll
-      for (int g = 1; g < 8; ++g) lwmax = fmaxf(lwmax, lwg[g]);
-      // every row has a real key in slot 0 of the tile, so the bound is finite
+      for (int g = 1; g < 4 * HB; ++g) lwmax = fmaxf(lwmax, lwg[g]);
+      // every row has a real key in the first slot of this wave's part of the tile (a
+      // part holding only padding is skipped above), so the bound is finite
       const float mn = fmaxf(m, pair_max(__builtin_fmaf(amax, c2, lwmax)));
       const float alpha = fast_exp2(m - mn);  // 0 on the first tile (m = -inf)
       l *= alpha;
@@ -327,16 +348,16 @@ void attn_fwd_bf16(Dims P, const uint16_t* __restrict__ q, const uint16_t* __res
       probs();
     }
     l += ps;
-    // O^T += V^T P^T over four 16-slot groups; D/32 independent accumulators. The
+    // O^T += V^T P^T over this wave's 16-slot groups; D/32 independent accumulators. The
     // wave raises its issue priority for these products, so on a SIMD shared with a
     // wave that is in its softmax the matrix core is fed first and the other wave's
     // VALU work fills the gaps.
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-    for (int i = 0; i < 4 * kVdb; ++i) {
+    for (int i = 0; i < 2 * HB * kVdb; ++i) {
       o[i % kVdb] = mfma32x32x16(as_bf16x8(vf[i % kVdb]), pb[i / kVdb], o[i % kVdb]);
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 1);
-      if (i + kVdb < 4 * kVdb) {
+      if (i + kVdb < 2 * HB * kVdb) {
         vread(i + kVdb);
         __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 1);
       }
@@ -348,6 +369,42 @@ void attn_fwd_bf16(Dims P, const uint16_t* __restrict__ q, const uint16_t* __res
     if (t + 1 < ntiles) step(t + 1, k1s, v1s, k0s, v0s);
   }
 
+  if constexpr (Cfg::kSplit) {
+    // merge the two slot halves of each row: the second-half wave of a row pair hands
+    // its reference, sum and O^T to the first through LDS (the K stages, now free)
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    float4* xo = reinterpret_cast<float4*>(qsel ? k1s : k0s);  // 16 KB per row pair
+    float* xm = reinterpret_cast<float*>(qsel ? v1s : v0s);
+    if (sh == 1) {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          xo[(db * 4 + q4) * 64 + lane] = make_float4(o[db][4 * q4], o[db][4 * q4 + 1], o[db][4 * q4 + 2], o[db][4 * q4 + 3]);
+      xm[lane] = m;
+      xm[64 + lane] = l;
+    }
+    __syncthreads();
+    if (sh == 1) return;
+    const float m1 = xm[lane], l1 = xm[64 + lane];
+    const float mt = fmaxf(m, m1);
+    // a half that never saw a real key keeps m = -inf and contributes nothing
+    const float f0 = mt == -__builtin_inff() ? 0.0f : fast_exp2(m - mt);
+    const float f1 = mt == -__builtin_inff() ? 0.0f : fast_exp2(m1 - mt);
+    l = l * f0 + l1 * f1;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 x = xo[(db * 4 + q4) * 64 + lane];
+        o[db][4 * q4 + 0] = o[db][4 * q4 + 0] * f0 + x.x * f1;
+        o[db][4 * q4 + 1] = o[db][4 * q4 + 1] * f0 + x.y * f1;
+        o[db][4 * q4 + 2] = o[db][4 * q4 + 2] * f0 + x.z * f1;
+        o[db][4 * q4 + 3] = o[db][4 * q4 + 3] * f0 + x.w * f1;
+      }
+    m = mt;
+  }
   // epilogue: O^T lane layout -> row qr, dims db*32 + (e/4)*8 + half*4 + e%4
   if (qr < n) {
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;

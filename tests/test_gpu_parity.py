@@ -512,6 +512,11 @@ EDGE = [
     (1, 1, 128, 128, 32, 8, 4, 0.5),  # one token: one row, one cluster, one sub-block
     (17, 2, 64, 64, 32, 4, 3, 1.0),  # fewer tokens than one key sub-block
     (1000, 2, 128, 128, 32, 16, 16, 0.3),  # 16 clusters (their own assembly kernel), 16 iterations
+    # q_block 64 at d 128 (four waves, each with one 32-slot half of every tile)
+    (20, 1, 128, 64, 16, 4, 2, 1.0),  # one tile whose second half is all padding
+    (1000, 2, 128, 64, 32, 8, 4, 0.3),
+    (777, 1, 128, 64, 64, 8, 4, 1.0),
+    (600, 2, 128, 64, 128, 8, 3, 0.4),
 ]
 
 
@@ -1038,6 +1043,7 @@ INTRA_SHAPES = [
     (2048, 1, 128, 128, 64, 512),
     (1000, 1, 128, 128, 128, 0),
     (300, 1, 128, 128, 32, 512),  # one neighbourhood: Gather is dense, Scatter block-diagonal
+    (700, 1, 128, 64, 32, 128),
 ]
 
 
