@@ -118,7 +118,7 @@ void attn_fwd_bf16(Dims P, const uint16_t* __restrict__ q, const uint16_t* __res
   const __amdgpu_buffer_rsrc_t rv =
       __builtin_amdgcn_make_buffer_rsrc((void*)(v + size_t(bh) * N * D), (short)0, head_bytes, 0x00020000);
 
-  // Q^T as the B operand: lane -> query row (wave*32 + col), 8 dims per k step
+  // Q^T as the B operand: lane -> query row (qsel*32 + col), 8 dims per k step
   const int qr = qsel * 32 + col;
   bf16x8_t qf[D / 16];
   {
