@@ -75,12 +75,33 @@ __device__ __forceinline__ T block_sum(T v, T* red) {
   return t;
 }
 
-// floor(num / den) for num < 2^62, den < 2^40, via one fp64 division and an exact fix-up.
-__device__ __forceinline__ uint64_t udiv_floor(uint64_t num, uint64_t den) {
-  uint64_t q = uint64_t(double(num) / double(den));
-  while (q * den > num) --q;
-  while ((q + 1) * den <= num) ++q;
-  return q;
+// The water-filling test room * w >= S for every uncapped w of a row, as one bound per
+// pass: for an integer w >= 0 it holds iff w >= ceil(S / room) (room > 0), and with
+// room = 0 iff S = 0. The fp64 quotient is within one of the integer one; the
+// fix-ups make it exact. Bounds past 2^32 - 1 are clamped (every w is below 2^25).
+__device__ __forceinline__ uint32_t cap_bound(uint64_t S, uint64_t room) {
+  if (room == 0) return S == 0 ? 0u : 0xFFFFFFFFu;
+  uint64_t W = uint64_t(double(S) / double(room));
+  while (W * room < S) ++W;
+  while (W > 0 && (W - 1) * room >= S) --W;
+  return W > 0xFFFFFFFFull ? 0xFFFFFFFFu : uint32_t(W);
+}
+
+// The threshold floor(room * w * 2^24 / S) of an uncapped w (room * w < S, so it is below
+// 2^24). R = room * 2^24 / S in fp64 (both exact, one rounding), and w * R (one more
+// rounding) lies within 2^-28 of the quotient, so its integer part is the floor unless
+// the fraction lies within 2^-27 of an integer; there an exact integer comparison
+// decides between the two candidates.
+__device__ __forceinline__ uint32_t threshold_floor(uint32_t w, uint64_t room, uint64_t S, double R) {
+  const double y = double(w) * R;
+  uint32_t t = uint32_t(y);
+  const double fr = y - double(t);
+  if (fr < 0x1p-27 || fr > 1.0 - 0x1p-27) {
+    const uint64_t num = room * uint64_t(w) * uint64_t(kOne);
+    if (uint64_t(t + 1) * S <= num) ++t;
+    else if (uint64_t(t) * S > num) --t;
+  }
+  return t;
 }
 
 __global__ __launch_bounds__(kThreads) void sample_kernel(Dims P, int K, uint32_t seed_lo, uint32_t seed_hi,
@@ -125,11 +146,12 @@ __global__ __launch_bounds__(kThreads) void sample_kernel(Dims P, int K, uint32_
         if (!((capped[j >> 5] >> (j & 31)) & 1u)) part += quantize(s[j]);
       S = block_sum<uint64_t>(part, red64);
       room = uint64_t(K - m);
+      const uint32_t W = cap_bound(S, room);  // room * w >= S  <=>  w >= W
       __syncthreads();
       int nnew = 0;
       for (int j = tid; j < nkb; j += kThreads) {
         if (!((capped[j >> 5] >> (j & 31)) & 1u)) {
-          if (room * quantize(s[j]) >= S) {
+          if (quantize(s[j]) >= W) {
             atomicOr(&capped[j >> 5], 1u << (j & 31));
             ++nnew;
           }
@@ -143,6 +165,7 @@ __global__ __launch_bounds__(kThreads) void sample_kernel(Dims P, int K, uint32_
   }
 
   // ---- draw, compaction, outputs ----
+  const double R = double(room * uint64_t(kOne)) / double(S);
   if (tid == 0) scan_base = 0;
   __syncthreads();
   const size_t out0 = size_t(row) * nkb;
@@ -168,9 +191,8 @@ __global__ __launch_bounds__(kThreads) void sample_kernel(Dims P, int K, uint32_
             if ((cw >> bit) & 1u) {
               t = kOne;
             } else {
-              const uint64_t num = room * uint64_t(quantize(s[j])) * uint64_t(kOne);
-              const uint64_t q = udiv_floor(num, S);
-              t = q > 0 ? uint32_t(q) : 1u;
+              const uint32_t q = threshold_floor(quantize(s[j]), room, S, R);
+              t = q > 0 ? q : 1u;
             }
             tw[bit] = t;
             if ((rr[e] >> 8) < t) keep |= 1u << bit;
@@ -210,14 +232,6 @@ __global__ __launch_bounds__(kThreads) void sample_kernel(Dims P, int K, uint32_
 }
 
 
-// floor(num / S) for num < 2^64 with quotient below 2^25, given rS ~ 1/S:
-// the fp64 estimate is within one of the true floor, the fix-ups make it exact.
-__device__ __forceinline__ uint32_t floor_div_est(uint64_t num, uint64_t S, double rS) {
-  uint64_t q = uint64_t(double(num) * rS);
-  if (q * S > num) --q;
-  if ((q + 1) * S <= num) ++q;
-  return uint32_t(q);
-}
 
 __device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
@@ -323,13 +337,14 @@ __global__ __launch_bounds__(256) void sample_wave_kernel(Dims P, int K, int row
         for (int e = 0; e < kLaneElems; ++e) part += ((cap[c] >> e) & 1u) ? 0u : w[c][e];
       S = wave_sum_u64(uint64_t(part));
       room = uint64_t(K - m);
+      const uint32_t W = cap_bound(S, room);  // room * w >= S  <=>  w >= W
       int nnew = 0;
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
 #pragma unroll
         for (int e = 0; e < kLaneElems; ++e) {
           const bool un = ((valid[c] & ~cap[c]) >> e) & 1u;
-          if (un && room * uint64_t(w[c][e]) >= S) {
+          if (un && w[c][e] >= W) {
             cap[c] |= 1u << e;
             ++nnew;
           }
@@ -342,7 +357,7 @@ __global__ __launch_bounds__(256) void sample_wave_kernel(Dims P, int K, int row
   }
 
   // ---- draw: thresholds replace the weights in place ----
-  const double rS = 1.0 / double(S);
+  const double R = double(room * uint64_t(kOne)) / double(S);
   uint32_t keep[NCH];
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
@@ -350,7 +365,7 @@ __global__ __launch_bounds__(256) void sample_wave_kernel(Dims P, int K, int row
     for (int e = 0; e < kLaneElems; ++e) {
       uint32_t t = kOne;
       if (!((cap[c] >> e) & 1u)) {
-        const uint32_t q = floor_div_est(room * uint64_t(w[c][e]) * uint64_t(kOne), S, rS);
+        const uint32_t q = threshold_floor(w[c][e], room, S, R);
         t = q > 0u ? q : 1u;
       }
       w[c][e] = ((valid[c] >> e) & 1u) ? t : 0u;
@@ -486,13 +501,14 @@ __global__ __launch_bounds__(kThreads) void sample_block_kernel(Dims P, int K, u
         for (int e = 0; e < kLaneElems; ++e) part += ((cap[c] >> e) & 1u) ? 0u : w[c][e];
       S = block_sum<uint64_t>(uint64_t(part), red64);
       room = uint64_t(K - m);
+      const uint32_t W = cap_bound(S, room);  // room * w >= S  <=>  w >= W
       int nnew = 0;
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
 #pragma unroll
         for (int e = 0; e < kLaneElems; ++e) {
           const bool un = ((valid[c] & ~cap[c]) >> e) & 1u;
-          if (un && room * uint64_t(w[c][e]) >= S) {
+          if (un && w[c][e] >= W) {
             cap[c] |= 1u << e;
             ++nnew;
           }
@@ -505,7 +521,7 @@ __global__ __launch_bounds__(kThreads) void sample_block_kernel(Dims P, int K, u
   }
 
   // ---- draw: thresholds replace the weights in place ----
-  const double rS = 1.0 / double(S);
+  const double R = double(room * uint64_t(kOne)) / double(S);
   uint32_t keep[NCH];
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
@@ -513,7 +529,7 @@ __global__ __launch_bounds__(kThreads) void sample_block_kernel(Dims P, int K, u
     for (int e = 0; e < kLaneElems; ++e) {
       uint32_t t = kOne;
       if (!((cap[c] >> e) & 1u)) {
-        const uint32_t q = floor_div_est(room * uint64_t(w[c][e]) * uint64_t(kOne), S, rS);
+        const uint32_t q = threshold_floor(w[c][e], room, S, R);
         t = q > 0u ? q : 1u;
       }
       w[c][e] = ((valid[c] >> e) & 1u) ? t : 0u;
