@@ -47,8 +47,11 @@ def sanitized(tmp_path_factory):
     subprocess.run([b.hipcc(), *b.FLAGS, "-O1", "-g", *SAN, "-x", "hip", "-c", os.path.join(CSRC, "abi.cpp"),
                     "-o", abi_o], check=True, capture_output=True, text=True)
     lib = str(out / "libabattn_san.so")
-    subprocess.run([b.hipcc(), f"--offload-arch={b.ARCH}", "-shared", "-fPIC", "-fsanitize=address,undefined",
-                    "-shared-libsan", abi_o, *objs, "-o", lib], check=True, capture_output=True, text=True)
+    # host link (the objects already carry their device code) with the host clang
+    rocm_lib = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "lib")
+    subprocess.run([clang + "++", "-shared", "-fPIC", "-fsanitize=address,undefined", "-shared-libsan", abi_o, *objs,
+                    "-L" + rocm_lib, "-lamdhip64", "-Wl,-rpath," + rocm_lib, "-o", lib],
+                   check=True, capture_output=True, text=True)
     return {"lib": lib, "rt": rt, "clang": clang, "dir": str(out)}
 
 

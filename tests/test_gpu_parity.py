@@ -19,11 +19,13 @@ hold at any size are checked on every row.
 
 import math
 import os
+import time
 from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import pytest
 import torch
+from threadpoolctl import threadpool_limits
 
 import block_sparse_attention_ibcs_amd as ab
 import workloads
@@ -251,7 +253,9 @@ def check_attention_heads(run, heads):
             ok &= bool(lerr.max() <= tol["lse"])
             return (i, ok, float(err.max()), int((err > tol["o_abs"]).sum()))
 
-        with ThreadPoolExecutor(_THREADS) as ex:
+        # one BLAS thread per worker: the workers' matrix products would otherwise each
+        # start a full BLAS thread pool and oversubscribe the cores
+        with threadpool_limits(1), ThreadPoolExecutor(_THREADS) as ex:
             res = list(ex.map(one, range(w.nqb)))
         failed = [i for (i, ok, _, _) in res if not ok]
         assert not failed, ((b, h), failed[:10])
@@ -259,6 +263,20 @@ def check_attention_heads(run, heads):
         STRICT["elements"] += len(res) * w.q_block * w.d
         STRICT["beyond_plain_bound"] += sum(x for (_, _, _, x) in res)
     return worst
+
+
+def _oracle_scores_head(run, mu, sz, K):
+    """oracle.block_scores_many over every query block of one head, the blocks split into
+    parts computed on threads (each block's scores depend on that block alone)."""
+    w = run.w
+    n_rows = np.array([min(w.q_block, w.N - i * w.q_block) for i in range(w.nqb)])
+    parts = np.array_split(np.arange(w.nqb), max(1, min(_THREADS, w.nqb)))
+
+    def part(ix):
+        return block_scores_many(mu[ix], sz[ix], n_rows[ix], K, w.k_block, run.scale, w.dtype == "bf16", chunk=16)
+
+    with threadpool_limits(1), ThreadPoolExecutor(_THREADS) as ex:
+        return np.concatenate(list(ex.map(part, parts)), axis=0)
 
 
 def check_independent_masks(run, heads, mu_all, sz_all):
@@ -270,9 +288,7 @@ def check_independent_masks(run, heads, mu_all, sz_all):
     The CPU scores are also within the score tolerance of the GPU's on every row."""
     w = run.w
     tol = TOL[w.dtype]
-    n_rows = np.array([min(w.q_block, w.N - i * w.q_block) for i in range(w.nqb)])
-    s_cpu = np.stack([block_scores_many(mu_all[b, h], sz_all[b, h], n_rows, run.k[b, h], w.k_block, run.scale,
-                                        w.dtype == "bf16") for (b, h) in heads])
+    s_cpu = np.stack([_oracle_scores_head(run, mu_all[b, h], sz_all[b, h], run.k[b, h]) for (b, h) in heads])
     s_gpu = np.stack([run.scores[b, h] for (b, h) in heads])
     lim = tol["score_abs"] + tol["score_rel"] * np.abs(s_cpu.astype(np.float64))
     assert np.all(np.abs(s_gpu.astype(np.float64) - s_cpu) <= lim)
@@ -346,18 +362,25 @@ def test_video_workload_full_path(name):
     the oracle on every query block of the first and the last head, and on sampled
     blocks of the others; independent CPU masks (P10) on every row of the first and
     last head (all heads of the 12-head shape)."""
+    clock = [("start", time.time())]
     run = _run(name)
+    clock.append(("inputs and GPU run", time.time()))
     w = run.w
     blocks = run.blocks(24)
     mu_all, sz_all = check_kmeans_every_block(run)
+    clock.append(("k-means", time.time()))
     check_scores(run, blocks)
+    clock.append(("scores", time.time()))
     rows = check_sampler_every_row(run.scores, run.density, run.seed, run.idx, run.wts, run.cnt, run.mask, tag=name)
     check_sampler_any_size(run)
+    clock.append(("sampler", time.time()))
     heads = [(0, 0), (w.B - 1, w.H - 1)]
     worst = check_attention_heads(run, heads)
     worst = max(worst, check_attention(run, [x for x in blocks if (x[0], x[1]) not in heads]))
+    clock.append(("attention", time.time()))
     p10_heads = [(b, h) for b in range(w.B) for h in range(w.H)] if w.H <= 12 else heads
     flips, expected, entries = check_independent_masks(run, p10_heads, mu_all, sz_all)
+    clock.append(("independent masks", time.time()))
     # realised density is close to the target (Poisson sampling around K per row)
     K = max(1, min(w.nkb, math.floor(run.density * w.nkb + 0.5)))
     assert abs(run.cnt.mean() - K) < 0.05 * K + 1
@@ -365,7 +388,8 @@ def test_video_workload_full_path(name):
           f"attention on every block of {len(heads)} heads, worst |err| {worst:.3e}; "
           f"independent masks: {flips} flips in {entries} entries (expected {expected:.2f}); "
           f"mean kept {run.cnt.mean():.1f} of K={K}; "
-          f"elements past the plain 2e-2 so far: {STRICT['beyond_plain_bound']} of {STRICT['elements']}")
+          f"elements past the plain 2e-2 so far: {STRICT['beyond_plain_bound']} of {STRICT['elements']}; seconds: "
+          + ", ".join(f"{k} {t1 - t0:.1f}" for (_, t0), (k, t1) in zip(clock, clock[1:])))
 
 
 class _ScoreRows:

@@ -31,6 +31,8 @@ from __future__ import annotations
 
 import dataclasses
 import math
+import os
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
@@ -108,7 +110,8 @@ def _field(rng: np.random.Generator, H: int, d: int, grid, amplitude: float) -> 
     x = np.arange(W, dtype=np.float64)
     amp = np.float32(amplitude * math.sqrt(2.0 / 4.0))
     out = np.zeros((H, T, Hg, W, d), dtype=np.float32)
-    for h in range(H):
+
+    def head(h):  # every random number is drawn above, so heads are independent
         for r in range(4):
             kt, ky, kx = freqs[h, :, r, 0], freqs[h, :, r, 1], freqs[h, :, r, 2]
             # angle = 2*pi*(kt t/T + ky y/Hg + kx x/W) + phi, split as a (t, y) part and an x part
@@ -122,6 +125,11 @@ def _field(rng: np.random.Generator, H: int, d: int, grid, amplitude: float) -> 
             out[h] += s_ty * c_x
             out[h] += c_ty * s_x
         out[h] *= amp
+
+    # the heads on threads (numpy releases the interpreter lock in these array
+    # operations); each head's values are the same as in a sequential loop
+    with ThreadPoolExecutor(max(1, min(16, os.cpu_count() or 1, H))) as ex:
+        list(ex.map(head, range(H)))
     return out.reshape(H, T * Hg * W, d)
 
 
