@@ -91,7 +91,8 @@ __device__ __forceinline__ uint32_t cap_bound(uint64_t S, uint64_t room) {
 // 2^24). R = room * 2^24 / S in fp64 (both exact, one rounding), and w * R (one more
 // rounding) lies within 2^-28 of the quotient, so its integer part is the floor unless
 // the fraction lies within 2^-27 of an integer; there an exact integer comparison
-// decides between the two candidates.
+// decides between the two candidates (room * w * 2^24 < S * 2^24 <= 65536 * 2^48: rows
+// hold at most 65536 sub-blocks, so the product fits 64 bits).
 __device__ __forceinline__ uint32_t threshold_floor(uint32_t w, uint64_t room, uint64_t S, double R) {
   const double y = double(w) * R;
   uint32_t t = uint32_t(y);
