@@ -431,7 +431,7 @@ __global__ __launch_bounds__(128) void attn_fwd_f32(Dims P, const float* __restr
                                                     const float* __restrict__ weights,
                                                     const int32_t* __restrict__ counts, float* __restrict__ out,
                                                     float* __restrict__ lse, const int32_t* __restrict__ order) {
-  constexpr int TS = 32;
+  constexpr int TS = 32, CH = 8;
   __shared__ float Kt[TS][D];
   __shared__ float Vv[TS][D];
   __shared__ int skey[TS];
@@ -483,19 +483,43 @@ __global__ __launch_bounds__(128) void attn_fwd_f32(Dims P, const float* __restr
       Vv[s][d] = key >= 0 ? v[(size_t(bh) * N + key) * D + d] : 0.0f;
     }
     __syncthreads();
-    for (int s = 0; s < TS; ++s) {
-      if (skey[s] < 0) continue;
-      float dot = 0.0f;
+    // The online softmax advances a chunk of CH keys at a time: the chunk's
+    // probabilities are summed among themselves before they meet the running
+    // sums, so a row's many small terms are not each rounded away against a
+    // large running l (a per-key update lost up to ~1e-5 of l that way).
+    for (int s0 = 0; s0 < TS; s0 += CH) {
+      float p[CH];
+      float tm = -__builtin_inff();
 #pragma unroll
-      for (int d = 0; d < D; ++d) dot = __builtin_fmaf(qv[d], Kt[s][d], dot);
-      const float x = __builtin_fmaf(dot, c2, slw[s]);
-      const float mn = fmaxf(m, x);
-      const float alpha = fast_exp2(m - mn);
-      const float pp = fast_exp2(x - mn);
-      l = l * alpha + pp;
+      for (int s = 0; s < CH; ++s) {
+        float x = -__builtin_inff();  // keys outside the sequence weigh nothing
+        if (skey[s0 + s] >= 0) {
+          float dot = 0.0f;
+#pragma unroll
+          for (int d = 0; d < D; ++d) dot = __builtin_fmaf(qv[d], Kt[s0 + s][d], dot);
+          x = __builtin_fmaf(dot, c2, slw[s0 + s]);
+        }
+        p[s] = x;
+        tm = fmaxf(tm, x);
+      }
+      if (tm == -__builtin_inff()) continue;  // the same for every thread: skey is shared
+      const float mn = fmaxf(m, tm);
+      const float alpha = fast_exp2(m - mn);  // 0 before the first key
+      float ps = 0.0f;
+#pragma unroll
+      for (int s = 0; s < CH; ++s) {
+        p[s] = fast_exp2(p[s] - mn);
+        ps += p[s];
+      }
+      l = __builtin_fmaf(l, alpha, ps);
       m = mn;
 #pragma unroll
-      for (int d = 0; d < D; ++d) o[d] = __builtin_fmaf(pp, Vv[s][d], o[d] * alpha);
+      for (int d = 0; d < D; ++d) {
+        float t = 0.0f;
+#pragma unroll
+        for (int s = 0; s < CH; ++s) t = __builtin_fmaf(p[s], Vv[s0 + s][d], t);
+        o[d] = __builtin_fmaf(o[d], alpha, t);
+      }
     }
   }
   if (r < n) {

@@ -631,6 +631,47 @@ def test_explicit_softmax_scale(scale, dtype):
     check_attention(run, blocks)
 
 
+def _random_configs(n, seed=2024):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        d = int(rng.choice([64, 128]))
+        bq = int(rng.choice([64, 128]))
+        out.append(dict(B=int(rng.integers(1, 3)), H=int(rng.integers(1, 3)), N=int(rng.integers(1, 1500)), d=d,
+                        Bq=bq, Bk=int(rng.choice([16, 32, 64, 128])), C=int(rng.integers(1, 17)),
+                        T=int(rng.integers(1, 9)), density=float(rng.choice([0.02, 0.1, 0.3, 0.7, 1.0])),
+                        dtype=str(rng.choice(["bf16", "fp32"])),
+                        scale=float(rng.choice([0.0, 0.0, 0.05, 0.2])), seed=int(rng.integers(0, 2**31))))
+    return out
+
+
+@pytest.mark.parametrize("cfg", _random_configs(24), ids=lambda c: "-".join(str(v) for v in c.values()))
+def test_random_configurations(cfg):
+    """Seeded random descriptors across the accepted space (batch, heads, length, both head
+    dims and query block sizes, every sub-block size, 1-16 clusters, 1-8 iterations,
+    densities 0.02-1, both dtypes, default or caller-given scale): every query block
+    through k-means, scores, the draw and attention against the oracle."""
+    _gpu()
+    c = cfg
+    w = workloads.Workload("random", c["B"], c["H"], (1, 1, c["N"]), c["d"], c["dtype"], c["Bq"], c["Bk"], c["C"],
+                           c["density"], 0.5, False, kmeans_iters=c["T"])
+    rng = np.random.default_rng(c["seed"])
+    shp = (c["B"], c["H"], c["N"], c["d"])
+    base = rng.standard_normal(shp).astype(np.float32)
+    q = (base + 0.5 * rng.standard_normal(shp)).astype(np.float32)
+    k = (base + 0.5 * rng.standard_normal(shp)).astype(np.float32)
+    v = rng.standard_normal(shp).astype(np.float32)
+    if c["dtype"] == "bf16":
+        q, k, v = (workloads.round_to_bf16(x) for x in (q, k, v))
+    run = Run(w, inputs=(q, k, v), seed=c["seed"] % 1000, scale=c["scale"])
+    blocks = run.blocks(10**6)
+    check_kmeans(run, blocks)
+    check_scores(run, blocks)
+    check_sampler(run, blocks)
+    check_sampler_any_size(run)
+    check_attention(run, blocks)
+
+
 BATCHED = [
     # (B, N, H, d, Bq, Bk, C, T, density, dtype): more than one batch entry
     (2, 700, 2, 128, 128, 32, 8, 4, 0.3, "bf16"),
