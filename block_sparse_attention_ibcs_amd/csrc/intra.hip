@@ -10,9 +10,10 @@
 // every kept sub-block, ascending lists.
 //
 // One workgroup per (b, h, query block). Entry e of a Gather row is sub-block
-// j0 + e of the neighbourhood's run; entry e of a Scatter row is sub-block t of
-// neighbourhood n (n = e / (Bq/Bk), t = e % (Bq/Bk)): every neighbourhood but the
-// last contributes all Bq/Bk of its sub-blocks at the block's offset.
+// j0 + e of the neighbourhood's run; with Bk <= Bq, entry e of a Scatter row is
+// sub-block t of neighbourhood n (n = e / (Bq/Bk), t = e % (Bq/Bk)): every
+// neighbourhood but the last contributes all Bq/Bk of its sub-blocks at the block's
+// offset; with Bk > Bq each neighbourhood's slice is one sub-block.
 #include "ab_internal.h"
 
 namespace ab {
@@ -31,6 +32,13 @@ __global__ __launch_bounds__(256) void intra_lists_kernel(Dims P, int layer, int
     j0 = (p * L) / Bk;
     const int end = min(N, (p + 1) * L);
     count = ceil_div(end, Bk) - j0;
+  } else if (Bk > Bq) {
+    // A slice of Bq tokens at a Bq-aligned offset lies inside one sub-block: one entry
+    // per neighbourhood whose slice holds real tokens, each a different sub-block when
+    // L >= Bk. L < Bk leaves L = Bq and offset 0, so consecutive slices pair up inside
+    // one sub-block and together cover the sequence: every sub-block.
+    const int ns = N > o ? ceil_div(N - o, L) : 0;
+    count = L >= Bk ? ns : P.nkb;
   } else {
     // neighbourhoods whose slice at offset o holds real tokens, and the sub-blocks of
     // the last one (possibly cut by the end of the sequence)
@@ -47,6 +55,8 @@ __global__ __launch_bounds__(256) void intra_lists_kernel(Dims P, int layer, int
     int j;
     if (layer == AB_INTRA_GATHER) {
       j = j0 + e;
+    } else if (Bk > Bq) {
+      j = L >= Bk ? (e * L + o) / Bk : e;
     } else {
       const int per = Bq / Bk;
       const int n = e / per, t = e % per;

@@ -1111,6 +1111,8 @@ INTRA_SHAPES = [
     (1000, 1, 128, 128, 128, 0),
     (300, 1, 128, 128, 32, 512),  # one neighbourhood: Gather is dense, Scatter block-diagonal
     (700, 1, 128, 64, 32, 128),
+    (700, 1, 128, 64, 128, 64),  # sub-blocks larger than query blocks: slices pair up, Scatter is dense
+    (913, 2, 64, 64, 128, 192),  # sub-blocks larger than query blocks, one per neighbourhood's slice
 ]
 
 
@@ -1147,6 +1149,39 @@ def test_intra_two_batch_entries(layer):
     run = _IntraRun(w, inputs, layer, L)
     _check_intra_lists(run, layer, L)
     check_attention(run, [(b, h, i) for b in range(2) for h in range(H) for i in range(w.nqb)])
+
+
+def _random_intra_configs(n, seed=77):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        bq = int(rng.choice([64, 128]))
+        out.append(dict(B=int(rng.integers(1, 3)), H=int(rng.integers(1, 3)), N=int(rng.integers(1, 2200)),
+                        d=int(rng.choice([64, 128])), Bq=bq, Bk=int(rng.choice([16, 32, 64, 128])),
+                        L=int(rng.choice([0, bq, 2 * bq, 3 * bq, 8 * bq])), layer=int(rng.integers(0, 2)),
+                        dtype=str(rng.choice(["bf16", "fp32"])), seed=int(rng.integers(0, 2**31))))
+    return out
+
+
+@pytest.mark.parametrize("cfg", _random_intra_configs(12), ids=lambda c: "-".join(str(v) for v in c.values()))
+def test_intra_random_configurations(cfg):
+    """Seeded random INTRA descriptors (batch, heads, length, both head dims, query block
+    sizes and dtypes, every sub-block size, neighbourhoods of one to eight query blocks or
+    the default, both layers): lists bit-exact and attention on every query block."""
+    c = cfg
+    w = workloads.Workload("intra", c["B"], c["H"], (1, 1, c["N"]), c["d"], c["dtype"], c["Bq"], c["Bk"], 8, 0.1, 0.5,
+                           False)
+    rng = np.random.default_rng(c["seed"])
+    shp = (c["B"], c["H"], c["N"], c["d"])
+    base = rng.standard_normal(shp).astype(np.float32)
+    inputs = ((base + 0.5 * rng.standard_normal(shp)).astype(np.float32),
+              (base + 0.5 * rng.standard_normal(shp)).astype(np.float32),
+              rng.standard_normal(shp).astype(np.float32))
+    if c["dtype"] == "bf16":
+        inputs = tuple(workloads.round_to_bf16(x) for x in inputs)
+    run = _IntraRun(w, inputs, c["layer"], c["L"])
+    _check_intra_lists(run, c["layer"], c["L"])
+    check_attention(run, [(b, h, i) for b in range(w.B) for h in range(w.H) for i in range(w.nqb)])
 
 
 @pytest.mark.parametrize("layer", [0, 1])
