@@ -780,10 +780,11 @@ def test_scorer_reference_paths():
                                          (4096, 0.5), (4100, 0.1), (4725, 0.08), (7425, 1.0), (9000, 0.05),
                                          (16384, 0.1), (20000, 0.02)])
 def test_sampler_rows_any_length(nkb, density):
-    """The sampler alone on synthetic score rows: short rows, each register-resident
-    row length class (one wave per row up to 4096 sub-blocks, one workgroup per row up
-    to 16384), and rows long enough for the LDS-bitset path; peaked rows force several
-    water-filling passes; zero, negative, NaN, sub-2^-24 and >= 1 scores."""
+    """The sampler alone on synthetic score rows, every row bit-exact against the
+    oracle: short rows, each register-resident row length class (one wave per row up
+    to 4096 sub-blocks, one workgroup per row up to 16384), and rows long enough for
+    the LDS-bitset path; peaked rows force several water-filling passes; zero,
+    negative, NaN, sub-2^-24 and >= 1 scores."""
     _gpu()
     Bk, Bq = 16, 128
     H = 1 if nkb > 16384 else 2
@@ -811,7 +812,7 @@ def test_sampler_rows_any_length(nkb, density):
     torch.cuda.synchronize()
     idx, wts, cnt = idx_d.cpu().numpy(), wts_d.cpu().numpy(), cnt_d.cpu().numpy()
     mask = mask_d.cpu().numpy().view(np.uint32)
-    keys = [(0, int(x) // desc.nqb, int(x) % desc.nqb) for x in r] + [(0, 0, 0), (0, H - 1, desc.nqb - 1)]
+    keys = [(0, h, i) for h in range(H) for i in range(desc.nqb)]  # every row (~1 ms each on the host)
     ref = sample_rows(sc, density, seed, keys)
     for key, o in ref.items():
         b, h, i = key
@@ -848,8 +849,9 @@ def test_kmeans_rounding_case(dim):
 @pytest.mark.parametrize("nkb,density", [(37, 0.3), (1024, 0.1), (1000, 1.0), (2363, 0.08), (4096, 0.5),
                                          (4725, 0.05), (9000, 0.1), (16384, 0.02)])
 def test_topk_rows_any_length(nkb, density):
-    """Top-K truncation on synthetic score rows, bit-exact against the oracle: coarse
-    score values make ties at the cut common; zero, negative, NaN and >= 1 scores."""
+    """Top-K truncation on synthetic score rows, every row bit-exact against the
+    oracle: coarse score values make ties at the cut common; zero, negative, NaN and
+    >= 1 scores."""
     _gpu()
     Bk, Bq, H = 16, 128, 2
     N = nkb * Bk - 5
@@ -870,7 +872,7 @@ def test_topk_rows_any_length(nkb, density):
     mask = mask_d.cpu().numpy().view(np.uint32)
     K = max(1, min(nkb, math.floor(density * nkb + 0.5)))
     assert np.all(cnt == K)
-    keys = [(0, int(x) // desc.nqb, int(x) % desc.nqb) for x in r] + [(0, 0, 0), (0, H - 1, desc.nqb - 1)]
+    keys = [(0, h, i) for h in range(H) for i in range(desc.nqb)]  # every row
     for key, o in topk_rows(sc, density, keys).items():
         b, h, i = key
         assert np.array_equal(idx[b, h, i, :K], o["idx"]), key
@@ -883,9 +885,9 @@ def test_topk_rows_any_length(nkb, density):
 @pytest.mark.parametrize("nkb,density", [(37, 0.3), (1024, 0.1), (1000, 1.0), (2363, 0.08), (4096, 0.5),
                                          (4725, 0.05), (7425, 0.08), (16384, 0.02)])
 def test_systematic_rows_any_length(nkb, density):
-    """Systematic draw on synthetic score rows, bit-exact against the oracle (indices,
-    weights, counts, mask bits) on every row-length class it takes; every row keeps
-    floor(T / 2^24) or one more block."""
+    """Systematic draw on synthetic score rows, every row bit-exact against the oracle
+    (indices, weights, counts, mask bits) on every row-length class it takes; every
+    row keeps floor(T / 2^24) or one more block."""
     _gpu()
     Bk, Bq, H = 16, 128, 2
     N = nkb * Bk - 9
@@ -907,7 +909,7 @@ def test_systematic_rows_any_length(nkb, density):
     torch.cuda.synchronize()
     idx, wts, cnt = idx_d.cpu().numpy(), wts_d.cpu().numpy(), cnt_d.cpu().numpy()
     mask = mask_d.cpu().numpy().view(np.uint32)
-    keys = [(0, int(x) // desc.nqb, int(x) % desc.nqb) for x in r] + [(0, 0, 0), (0, H - 1, desc.nqb - 1)]
+    keys = [(0, h, i) for h in range(H) for i in range(desc.nqb)]  # every row
     for key, o in sample_rows_systematic(sc, density, seed, keys).items():
         b, h, i = key
         c = int(cnt[b, h, i])
