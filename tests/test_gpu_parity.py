@@ -1186,6 +1186,37 @@ def test_intra_random_configurations(cfg):
     check_attention(run, [(b, h, i) for b in range(w.B) for h in range(w.H) for i in range(w.nqb)])
 
 
+def test_intra_lists_small_sweep():
+    """The list kernel's closed forms against the oracle on every small descriptor of a
+    grid: both query block sizes, every sub-block size, 40 sequence lengths (one token,
+    ragged and exact multiples), neighbourhoods of one to five query blocks and the
+    default, both layers; every row's list, count and weights, and the processing order."""
+    _gpu()
+    lengths = sorted({1, 2, 63, 64, 65, 127, 128, 129, 255, 256, 257, 383, 384, 511, 512, 513, 640, 700}
+                     | set(range(3, 2200, 97)))
+    cases = 0
+    for Bq in (64, 128):
+        for Bk in (16, 32, 64, 128):
+            for N in lengths:
+                desc = ab.Desc(1, 1, N, 128, ab.AB_BF16, Bq, Bk, 8)
+                for U in (0, 1, 2, 3, 5):
+                    L = U * Bq
+                    Lr = L or default_partition(N, Bq)
+                    for layer, name in ((ab.AB_INTRA_SCATTER, "scatter"), (ab.AB_INTRA_GATHER, "gather")):
+                        idx, wts, cnt, order = ab.ab_intra_lists(desc, layer, L, want_order=True,
+                                                                 device=torch.device("cuda:0"))
+                        idx, wts, cnt = idx.cpu().numpy()[0, 0], wts.cpu().numpy()[0, 0], cnt.cpu().numpy()[0, 0]
+                        ref_idx, _, ref_cnt = intra_lists(N, Bq, Bk, Lr, name)
+                        assert np.array_equal(cnt, ref_cnt), (Bq, Bk, N, L, name)
+                        for i in range(desc.nqb):
+                            c = ref_cnt[i]
+                            assert np.array_equal(idx[i, :c], ref_idx[i, :c]), (Bq, Bk, N, L, name, i)
+                            assert np.all(wts[i, :c] == 1.0), (Bq, Bk, N, L, name, i)
+                        assert np.array_equal(order.cpu().numpy(), intra_row_order(N, Bq, Lr, name)), (Bq, Bk, N, L)
+                        cases += 1
+    print(f"{cases} descriptors")
+
+
 @pytest.mark.parametrize("layer", [0, 1])
 @pytest.mark.parametrize("name", ["wan1.3b", "hunyuan"])
 def test_intra_video_shape(name, layer):
