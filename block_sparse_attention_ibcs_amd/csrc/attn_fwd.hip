@@ -456,6 +456,7 @@ __global__ __launch_bounds__(128) void attn_fwd_f32(Dims P, const float* __restr
     o[d] = 0.0f;
   }
   float m = -__builtin_inff(), l = 0.0f;
+  float lc = 0.0f;  // compensation of l (Kahan): the negated part of the last additions that l lost
   const float c2 = P.scale * kLog2e;
   const int total = cnt * Bk;
   for (int t0 = 0; t0 < total; t0 += TS) {
@@ -485,8 +486,10 @@ __global__ __launch_bounds__(128) void attn_fwd_f32(Dims P, const float* __restr
     __syncthreads();
     // The online softmax advances a chunk of CH keys at a time: the chunk's
     // probabilities are summed among themselves before they meet the running
-    // sums, so a row's many small terms are not each rounded away against a
-    // large running l (a per-key update lost up to ~1e-5 of l that way).
+    // sums, and l takes the chunk sums with compensated (Kahan) addition, so a
+    // row's many small terms are not rounded away against a large running l (one
+    // key at a time that lost up to 2e-5 of l; chunks alone still 2e-5 on rows of
+    // a few thousand keys).
     for (int s0 = 0; s0 < TS; s0 += CH) {
       float p[CH];
       float tm = -__builtin_inff();
@@ -511,7 +514,12 @@ __global__ __launch_bounds__(128) void attn_fwd_f32(Dims P, const float* __restr
         p[s] = fast_exp2(p[s] - mn);
         ps += p[s];
       }
-      l = __builtin_fmaf(l, alpha, ps);
+      l *= alpha;
+      lc *= alpha;
+      const float y = ps - lc;
+      const float ls = l + y;
+      lc = (ls - l) - y;
+      l = ls;
       m = mn;
 #pragma unroll
       for (int d = 0; d < D; ++d) {
@@ -522,6 +530,7 @@ __global__ __launch_bounds__(128) void attn_fwd_f32(Dims P, const float* __restr
       }
     }
   }
+  l -= lc;
   if (r < n) {
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;
 #pragma unroll
