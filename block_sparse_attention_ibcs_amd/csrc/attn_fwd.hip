@@ -424,16 +424,24 @@ void attn_fwd_bf16(Dims P, const uint16_t* __restrict__ q, const uint16_t* __res
   }
 }
 
-// fp32 inputs: one thread per query row, VALU dot products against LDS tiles.
+// fp32 inputs: two threads per query row (lanes 2r and 2r + 1), each holding one half
+// of the row's dims of q and of the output; the pair adds its two half dot products
+// (a DPP swap of neighbouring lanes, the same sum in both). VALU products against LDS
+// tiles of TS keys. The online softmax advances CH keys at a time (the chunk's
+// probabilities summed among themselves first) and keeps the row sum and the output
+// in fp64, which runs at the fp32 vector rate here: fp32 running sums rounded a long
+// row's many small terms away (up to 2e-5 of the output on rows of a few thousand
+// keys, more on longer ones).
 template <int D>
-__global__ __launch_bounds__(128) void attn_fwd_f32(Dims P, const float* __restrict__ q, const float* __restrict__ k,
+__global__ __launch_bounds__(256) void attn_fwd_f32(Dims P, const float* __restrict__ q, const float* __restrict__ k,
                                                     const float* __restrict__ v, const int32_t* __restrict__ idx,
                                                     const float* __restrict__ weights,
                                                     const int32_t* __restrict__ counts, float* __restrict__ out,
                                                     float* __restrict__ lse, const int32_t* __restrict__ order) {
-  constexpr int TS = 32, CH = 8;
-  __shared__ float Kt[TS][D];
-  __shared__ float Vv[TS][D];
+  constexpr int TS = 32, CH = 8, HD = D / 2;
+  constexpr int RS = D + 2;  // LDS row: the second half starts one word late (another bank)
+  __shared__ float Kt[TS][RS];
+  __shared__ float Vv[TS][RS];
   __shared__ int skey[TS];
   __shared__ float slw[TS];
   int blk = blockIdx.x;
@@ -448,15 +456,17 @@ __global__ __launch_bounds__(128) void attn_fwd_f32(Dims P, const float* __restr
   const int cnt = min(max(counts[blk], 0), P.nkb);  // clamped to the row
   const int32_t* list = idx + size_t(blk) * P.nkb;
   const float* wl = weights + size_t(blk) * P.nkb;
-  const int r = threadIdx.x;
-  float qv[D], o[D];
+  const int r = threadIdx.x >> 1, hv = threadIdx.x & 1;
+  const int hoff = hv * (HD + 1);  // this thread's half of an LDS row
+  float qv[HD];
+  double o[HD];
 #pragma unroll
-  for (int d = 0; d < D; ++d) {
-    qv[d] = (r < n) ? q[(size_t(bh) * N + row0 + r) * D + d] : 0.0f;
-    o[d] = 0.0f;
+  for (int d = 0; d < HD; ++d) {
+    qv[d] = (r < n) ? q[(size_t(bh) * N + row0 + r) * D + hv * HD + d] : 0.0f;
+    o[d] = 0.0;
   }
-  float m = -__builtin_inff(), l = 0.0f;
-  float lc = 0.0f;  // compensation of l (Kahan): the negated part of the last additions that l lost
+  float m = -__builtin_inff();
+  double l = 0.0;
   const float c2 = P.scale * kLog2e;
   const int total = cnt * Bk;
   for (int t0 = 0; t0 < total; t0 += TS) {
@@ -480,62 +490,54 @@ __global__ __launch_bounds__(128) void attn_fwd_f32(Dims P, const float* __restr
     for (int p = threadIdx.x; p < TS * D; p += blockDim.x) {
       const int s = p / D, d = p % D;
       const int key = skey[s];
-      Kt[s][d] = key >= 0 ? k[(size_t(bh) * N + key) * D + d] : 0.0f;
-      Vv[s][d] = key >= 0 ? v[(size_t(bh) * N + key) * D + d] : 0.0f;
+      const int c = d < HD ? d : d + 1;
+      Kt[s][c] = key >= 0 ? k[(size_t(bh) * N + key) * D + d] : 0.0f;
+      Vv[s][c] = key >= 0 ? v[(size_t(bh) * N + key) * D + d] : 0.0f;
     }
     __syncthreads();
-    // The online softmax advances a chunk of CH keys at a time: the chunk's
-    // probabilities are summed among themselves before they meet the running
-    // sums, and l takes the chunk sums with compensated (Kahan) addition, so a
-    // row's many small terms are not rounded away against a large running l (one
-    // key at a time that lost up to 2e-5 of l; chunks alone still 2e-5 on rows of
-    // a few thousand keys).
     for (int s0 = 0; s0 < TS; s0 += CH) {
       float p[CH];
       float tm = -__builtin_inff();
 #pragma unroll
       for (int s = 0; s < CH; ++s) {
         float x = -__builtin_inff();  // keys outside the sequence weigh nothing
-        if (skey[s0 + s] >= 0) {
+        if (skey[s0 + s] >= 0) {      // the same for every thread: skey is shared
           float dot = 0.0f;
 #pragma unroll
-          for (int d = 0; d < D; ++d) dot = __builtin_fmaf(qv[d], Kt[s0 + s][d], dot);
-          x = __builtin_fmaf(dot, c2, slw[s0 + s]);
+          for (int d = 0; d < HD; ++d) dot = __builtin_fmaf(qv[d], Kt[s0 + s][hoff + d], dot);
+          // quad_perm [1, 0, 3, 2]: the neighbouring lane's half (every lane is active)
+          const float other = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(dot), 0xB1, 0xF, 0xF, false));
+          x = __builtin_fmaf(dot + other, c2, slw[s0 + s]);
         }
         p[s] = x;
         tm = fmaxf(tm, x);
       }
-      if (tm == -__builtin_inff()) continue;  // the same for every thread: skey is shared
+      if (tm == -__builtin_inff()) continue;  // no key of the sequence in this chunk (uniform)
       const float mn = fmaxf(m, tm);
-      const float alpha = fast_exp2(m - mn);  // 0 before the first key
+      const double alpha = fast_exp2(m - mn);  // 0 before the first key
       float ps = 0.0f;
 #pragma unroll
       for (int s = 0; s < CH; ++s) {
         p[s] = fast_exp2(p[s] - mn);
         ps += p[s];
       }
-      l *= alpha;
-      lc *= alpha;
-      const float y = ps - lc;
-      const float ls = l + y;
-      lc = (ls - l) - y;
-      l = ls;
+      l = __builtin_fma(l, alpha, double(ps));
       m = mn;
 #pragma unroll
-      for (int d = 0; d < D; ++d) {
+      for (int d = 0; d < HD; ++d) {
         float t = 0.0f;
 #pragma unroll
-        for (int s = 0; s < CH; ++s) t = __builtin_fmaf(p[s], Vv[s0 + s][d], t);
-        o[d] = __builtin_fmaf(o[d], alpha, t);
+        for (int s = 0; s < CH; ++s) t = __builtin_fmaf(p[s], Vv[s0 + s][hoff + d], t);
+        o[d] = __builtin_fma(o[d], alpha, double(t));
       }
     }
   }
-  l -= lc;
   if (r < n) {
-    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    const double inv = l > 0.0 ? 1.0 / l : 0.0;
 #pragma unroll
-    for (int d = 0; d < D; ++d) out[(size_t(bh) * N + row0 + r) * D + d] = o[d] * inv;
-    if (lse) lse[size_t(bh) * N + row0 + r] = l > 0.0f ? (m + fast_log2(l)) * kLn2 : -__builtin_inff();
+    for (int d = 0; d < HD; ++d) out[(size_t(bh) * N + row0 + r) * D + hv * HD + d] = float(o[d] * inv);
+    if (lse && hv == 0)
+      lse[size_t(bh) * N + row0 + r] = l > 0.0 ? (m + fast_log2(float(l))) * kLn2 : -__builtin_inff();
   }
 }
 
@@ -577,10 +579,11 @@ hipError_t launch_attn_fwd(const Dims& P, const void* q, const void* k, const vo
   auto Kp = static_cast<const float*>(k);
   auto Vp = static_cast<const float*>(v);
   auto O = static_cast<float*>(out);
+  // two threads per query row
   if (P.d == 128)
-    hipLaunchKernelGGL(attn_fwd_f32<128>, grid, dim3(P.Bq), 0, s, P, Q, Kp, Vp, idx, weights, counts, O, lse, order);
+    hipLaunchKernelGGL(attn_fwd_f32<128>, grid, dim3(2 * P.Bq), 0, s, P, Q, Kp, Vp, idx, weights, counts, O, lse, order);
   else
-    hipLaunchKernelGGL(attn_fwd_f32<64>, grid, dim3(P.Bq), 0, s, P, Q, Kp, Vp, idx, weights, counts, O, lse, order);
+    hipLaunchKernelGGL(attn_fwd_f32<64>, grid, dim3(2 * P.Bq), 0, s, P, Q, Kp, Vp, idx, weights, counts, O, lse, order);
   return hipGetLastError();
 }
 

@@ -691,6 +691,34 @@ def test_fp32_long_rows(cfg):
     test_random_configurations(cfg)
 
 
+@pytest.mark.parametrize("N,d,scale", [(20000, 64, 0.25), (20000, 128, 0.12), (40000, 64, 0.2)])
+def test_fp32_very_long_rows(N, d, scale):
+    """fp32 attention over every key of rows of 20000-40000 keys (lists of every
+    sub-block, weight 1) with peaked softmax rows: sampled query blocks within 1e-5 of
+    exact dense attention (the row sum and output accumulate in fp64)."""
+    _gpu()
+    rng = np.random.default_rng(N + d)
+    base = rng.standard_normal((1, 1, N, d)).astype(np.float32)
+    q = (base + 0.5 * rng.standard_normal((1, 1, N, d))).astype(np.float32)
+    k = (base + 0.5 * rng.standard_normal((1, 1, N, d))).astype(np.float32)
+    v = rng.standard_normal((1, 1, N, d)).astype(np.float32)
+    qd, kd, vd = (torch.from_numpy(x).cuda() for x in (q, k, v))
+    desc = ab.Desc.for_tensor(qd, 64, 64, 8, scale=scale)
+    nqb, nkb = desc.nqb, desc.nkb
+    idx = torch.arange(nkb, dtype=torch.int32).repeat(1, 1, nqb, 1).cuda()
+    wts = torch.ones((1, 1, nqb, nkb), dtype=torch.float32).cuda()
+    cnt = torch.full((1, 1, nqb), nkb, dtype=torch.int32).cuda()
+    out, lse = ab.ab_attn_fwd(desc, qd, kd, vd, idx, wts, cnt)
+    torch.cuda.synchronize()
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    for i in (0, nqb // 2, nqb - 1):
+        lo, hi = i * 64, min(N, (i + 1) * 64)
+        o_ref, lse_ref = dense_attention(q[0, 0, lo:hi], k[0, 0], v[0, 0], scale)
+        err = np.abs(out[0, 0, lo:hi] - o_ref)
+        assert err.max() <= 1e-5 + 2.0**-24 * np.abs(o_ref).max(), (i, float(err.max()))
+        assert np.abs(lse[0, 0, lo:hi] - lse_ref).max() <= 1e-5 * max(1.0, np.abs(lse_ref).max()), i
+
+
 BATCHED = [
     # (B, N, H, d, Bq, Bk, C, T, density, dtype): more than one batch entry
     (2, 700, 2, 128, 128, 32, 8, 4, 0.3, "bf16"),
