@@ -270,16 +270,19 @@ __global__ __launch_bounds__(256) void score_lse_f32(Dims P, const float* __rest
     eb[size_t(j) * C + c] = m + fast_log2(s);
   }
   __syncthreads();
-  // pass 2: each row's log-sum-exp over its sub-blocks (single split)
+  // pass 2: each row's log-sum-exp over its sub-blocks (single split); the running
+  // sum is kept in fp64 so that the many small terms of a long row are not rounded
+  // away against it (in fp32, NKB additions can lose up to NKB * 2^-24 of the sum)
   for (int c = threadIdx.x; c < C; c += blockDim.x) {
-    float m = -__builtin_inff(), s = 0.0f;
+    float m = -__builtin_inff();
+    double s = 0.0;
     for (int j = 0; j < P.nkb; ++j) {
       const float x = eb[size_t(j) * C + c];
       const float nm = fmaxf(m, x);
-      s = s * fast_exp2(m - nm) + fast_exp2(x - nm);
+      s = __builtin_fma(s, double(fast_exp2(m - nm)), double(fast_exp2(x - nm)));
       m = nm;
     }
-    lpart[(size_t(bh) * P.mrows + i * C + c)] = m + fast_log2(s);
+    lpart[(size_t(bh) * P.mrows + i * C + c)] = m + fast_log2(float(s));
   }
 }
 

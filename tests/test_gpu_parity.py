@@ -719,6 +719,32 @@ def test_fp32_very_long_rows(N, d, scale):
         assert np.abs(lse[0, 0, lo:hi] - lse_ref).max() <= 1e-5 * max(1.0, np.abs(lse_ref).max()), i
 
 
+@pytest.mark.parametrize("N,Bk", [(118800, 16), (40000, 32)])
+def test_fp32_scores_long_sequence(N, Bk):
+    """fp32 scores over sequences of 2500-7425 key sub-blocks (the HunyuanVideo length at
+    k_block 16): sampled query blocks within 1e-6 + 1e-4 s of the oracle, and every row
+    sums to 1."""
+    _gpu()
+    d = 64
+    rng = np.random.default_rng(N)
+    base = rng.standard_normal((1, 1, N, d)).astype(np.float32)
+    q = (base + 0.5 * rng.standard_normal((1, 1, N, d))).astype(np.float32)
+    k = (base + 0.5 * rng.standard_normal((1, 1, N, d))).astype(np.float32)
+    qd, kd = torch.from_numpy(q).cuda(), torch.from_numpy(k).cuda()
+    desc = ab.Desc.for_tensor(qd, 128, Bk, 8, 4)
+    scores = ab.ab_score(desc, qd, kd).cpu().numpy()
+    scale = 1.0 / math.sqrt(d)
+    for i in (0, desc.nqb // 3, desc.nqb - 1):
+        lo, hi = i * 128, min(N, (i + 1) * 128)
+        mu, sz, _ = kmeans_fp32(q[0, 0, lo:hi], 8, 4)
+        ref = block_scores(mu, sz, hi - lo, k[0, 0], Bk, scale, False).astype(np.float64)
+        err = np.abs(scores[0, 0, i].astype(np.float64) - ref)
+        lim = TOL["fp32"]["score_abs"] + TOL["fp32"]["score_rel"] * np.abs(ref)
+        assert np.all(err <= lim), (i, float((err / lim).max()))
+    sums = scores.astype(np.float64).sum(axis=-1)
+    assert np.all(np.abs(sums - 1.0) < 1e-4), float(np.abs(sums - 1).max())
+
+
 BATCHED = [
     # (B, N, H, d, Bq, Bk, C, T, density, dtype): more than one batch entry
     (2, 700, 2, 128, 128, 32, 8, 4, 0.3, "bf16"),
