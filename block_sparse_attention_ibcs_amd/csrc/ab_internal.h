@@ -29,12 +29,43 @@ __host__ __device__ constexpr int ceil_div(int a, int b) { return (a + b - 1) / 
 // logical ids, so neighbouring work items (which read overlapping data) share
 // an L2.
 constexpr int kXcds = 8;
-__device__ __forceinline__ int xcd_remap(int pid, int n) {
+__host__ __device__ inline int xcd_remap(int pid, int n) {
   const int xcd = pid % kXcds, local = pid / kXcds;
   const int per = (n + kXcds - 1) / kXcds;
   const int tall = n % kXcds;  // XCDs that receive `per` ids; the rest receive per - 1
   if (tall == 0 || xcd < tall) return xcd * per + local;
   return tall * per + (xcd - tall) * (per - 1) + local;
+}
+
+// Head-major variant for ids (b*H + h)*nqb + i over nbh = B*H heads: all XCDs work
+// on the same head at the same time, XCD x on its own contiguous slice of that
+// head's query blocks, then all move on to the next head. The keys and values in
+// use at any moment are then one or two heads' instead of about one head per XCD,
+// which matters once eight heads' K and V no longer fit the Infinity Cache. Each
+// head gives every XCD q = nqb / 8 blocks; its r = nqb % 8 extra blocks are dealt
+// round-robin over the XCDs, continuing from head to head, so XCD x receives
+// exactly as many ids as under xcd_remap (the first n % 8 XCDs one more) and the
+// map is a bijection on [0, nbh * nqb).
+__host__ __device__ inline int xcd_head_remap(int pid, int nbh, int nqb) {
+  const int x = pid % kXcds, j = pid / kXcds;  // XCD and position in its sequence
+  const int q = nqb / kXcds, r = nqb % kXcds;
+  // first position of head h in XCD x's sequence: h*q plus the extra blocks dealt
+  // to x by heads 0..h-1 (the integers below h*r congruent to x mod 8)
+  auto start = [&](int h) {
+    const long long e = (long long)h * r;
+    return h * q + (e > x ? int((e - x + kXcds - 1) / kXcds) : 0);
+  };
+  int h = int(((long long)j * kXcds) / ((long long)q * kXcds + r));
+  if (h > nbh - 1) h = nbh - 1;
+  while (h > 0 && start(h) > j) --h;
+  while (h + 1 < nbh && start(h + 1) <= j) ++h;
+  // head h deals its extras to the XCDs a, a+1, ..., a+r-1 (mod 8), a = h*r mod 8;
+  // XCD x's slice starts after x*q blocks and the extras of the XCDs below x
+  const int a = int(((long long)h * r) % kXcds);
+  int below;
+  if (a + r <= kXcds) below = min(max(x - a, 0), r);
+  else below = min(max(x - a, 0), kXcds - a) + min(x, a + r - kXcds);
+  return h * nqb + x * q + below + (j - start(h));
 }
 
 // Derived sizes of one problem.
