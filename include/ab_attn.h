@@ -270,6 +270,10 @@ int32_t ab_attn_fwd_ordered(const ab_desc* desc, const void* q, const void* k, c
  *            unique and in [0, NKB); counts in [0, NKB]).
  * out:     device [B, H, N, d], dtype of desc.
  * lse:     device fp32 [B, H, N] natural-log log-sum-exp; may be NULL.
+ * The outputs do not depend on the order in which query blocks are processed. Each
+ * XCD takes one contiguous range of (b, h, i) rows, unless eight heads' K and V
+ * exceed 256 MiB (the Infinity Cache; N > 65536 at d = 128): then all XCDs work on
+ * the same head at a time, each on its own slice of its query blocks.
  */
 int32_t ab_attn_fwd(const ab_desc* desc, const void* q, const void* k, const void* v,
                     const int32_t* idx, const float* weights, const int32_t* counts,
