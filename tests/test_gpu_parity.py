@@ -1308,37 +1308,39 @@ def test_intra_video_shape(name, layer):
     check_attention(run, Run.blocks(run, max_blocks=12))
 
 
-@pytest.mark.parametrize("B,H,N", [(1, 3, 70000), (2, 2, 66000)])
-def test_head_major_launch(B, H, N):
+@pytest.mark.parametrize("B,H,N,d,Bq,Bk", [(1, 3, 70000, 128, 128, 32), (2, 2, 66000, 128, 128, 32),
+                                            (1, 2, 70000, 128, 64, 16), (1, 2, 140000, 64, 128, 64)])
+def test_head_major_launch(B, H, N, d, Bq, Bk):
     """Sequences long enough that eight heads' K and V exceed the 256 MiB Infinity Cache
-    (more than 65536 tokens at d 128) run ab_attn_fwd head-major: every XCD on the same
-    head at a time, each on its own slice of the query blocks. Every row is written
-    (the outputs start as NaN), equals bit for bit the same kernel in the contiguous
-    per-XCD order (ab_attn_fwd_ordered with the identity order), and the first, the
-    last and sampled query blocks of every head match the oracle."""
+    (more than 65536 tokens at d 128, 131072 at d 64) run ab_attn_fwd head-major: every
+    XCD on the same head at a time, each on its own slice of the query blocks (also in
+    the q_block 64 kernel, whose waves split each tile). Every row is written (the
+    outputs start as NaN), equals bit for bit the same kernel in the contiguous per-XCD
+    order (ab_attn_fwd_ordered with the identity order), and the first, the last and
+    sampled query blocks of every head match the oracle."""
     _gpu()
-    w = workloads.Workload("long", B, H, (1, 1, N), 128, "bf16", 128, 32, 8, 0.1, 0.5, False, kmeans_iters=4)
-    rng = np.random.default_rng(N + H)
-    base = rng.standard_normal((B, H, N, 128)).astype(np.float32)
-    q = workloads.round_to_bf16(base + 0.5 * rng.standard_normal((B, H, N, 128)).astype(np.float32))
-    k = workloads.round_to_bf16(base + 0.5 * rng.standard_normal((B, H, N, 128)).astype(np.float32))
-    v = workloads.round_to_bf16(rng.standard_normal((B, H, N, 128)).astype(np.float32))
+    w = workloads.Workload("long", B, H, (1, 1, N), d, "bf16", Bq, Bk, 8, 0.1, 0.5, False, kmeans_iters=4)
+    rng = np.random.default_rng(N + H + d + Bq)
+    base = rng.standard_normal((B, H, N, d)).astype(np.float32)
+    q = workloads.round_to_bf16(base + 0.5 * rng.standard_normal((B, H, N, d)).astype(np.float32))
+    k = workloads.round_to_bf16(base + 0.5 * rng.standard_normal((B, H, N, d)).astype(np.float32))
+    v = workloads.round_to_bf16(rng.standard_normal((B, H, N, d)).astype(np.float32))
     del base
     run = Run(w, inputs=(q, k, v), seed=4)
-    d = run.desc
-    rows = d.B * d.H * d.nqb
+    desc = run.desc
+    rows = desc.B * desc.H * desc.nqb
     out = torch.full_like(run.out_d, float("nan"))
     lse = torch.full_like(run.lse_d, float("nan"))
-    ab.ab_attn_fwd(d, run.qd, run.kd, run.vd, run.idx_d, run.wts_d, run.cnt_d, out=out, lse=lse)
+    ab.ab_attn_fwd(desc, run.qd, run.kd, run.vd, run.idx_d, run.wts_d, run.cnt_d, out=out, lse=lse)
     ident = torch.arange(rows, dtype=torch.int32, device=out.device)
-    out_c, lse_c = ab.ab_attn_fwd_ordered(d, run.qd, run.kd, run.vd, run.idx_d, run.wts_d, run.cnt_d, ident)
+    out_c, lse_c = ab.ab_attn_fwd_ordered(desc, run.qd, run.kd, run.vd, run.idx_d, run.wts_d, run.cnt_d, ident)
     torch.cuda.synchronize()
     assert not torch.isnan(out).any() and not torch.isnan(lse).any()
     assert torch.equal(out, run.out_d) and torch.equal(lse, run.lse_d)
     assert torch.equal(out, out_c) and torch.equal(lse, lse_c)
-    blocks = sorted(set([(b, h, i) for b in range(B) for h in range(H) for i in (0, d.nqb - 1)] + run.blocks(12)))
+    blocks = sorted(set([(b, h, i) for b in range(B) for h in range(H) for i in (0, desc.nqb - 1)] + run.blocks(12)))
     worst = check_attention(run, blocks)
-    print(f"head-major B={B} H={H} N={N}: {rows} rows identical to the contiguous order; "
+    print(f"head-major B={B} H={H} N={N} d={d} Bq={Bq} Bk={Bk}: {rows} rows identical to the contiguous order; "
           f"{len(blocks)} blocks against the oracle, worst |err| {worst:.3e}")
 
 
