@@ -37,6 +37,9 @@ __host__ __device__ inline int xcd_remap(int pid, int n) {
   return tall * per + (xcd - tall) * (per - 1) + local;
 }
 
+// Capacity of the Infinity Cache (MALL) that the XCDs share.
+constexpr size_t kMallBytes = size_t(256) << 20;
+
 // Head-major variant for ids (b*H + h)*nqb + i over nbh = B*H heads: all XCDs work
 // on the same head at the same time, XCD x on its own contiguous slice of that
 // head's query blocks, then all move on to the next head. The keys and values in

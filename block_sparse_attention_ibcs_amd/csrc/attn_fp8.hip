@@ -59,7 +59,7 @@ void attn_fwd_fp8(Dims P, const uint8_t* __restrict__ qcode, const float* __rest
                   const uint8_t* __restrict__ vcode, const float* __restrict__ vscale,
                   const uint32_t* __restrict__ vms, const int32_t* __restrict__ idx,
                   const float* __restrict__ weights, const int32_t* __restrict__ counts,
-                  uint16_t* __restrict__ out, float* __restrict__ lse) {
+                  uint16_t* __restrict__ out, float* __restrict__ lse, int head_major) {
   using Cfg = Fp8Cfg<BK>;
   constexpr int kT = Cfg::kT;
   // separate LDS objects per stage: the gather landing in one stage never aliases
@@ -74,7 +74,9 @@ void attn_fwd_fp8(Dims P, const uint8_t* __restrict__ qcode, const float* __rest
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, col = lane & 31;
-  const int blk = xcd_remap(blockIdx.x, gridDim.x);  // (b*H + h)*nqb + i
+  // (b*H + h)*nqb + i, head-major when the gathered operands of eight heads exceed the
+  // Infinity Cache (as in the bf16 kernel)
+  const int blk = head_major ? xcd_head_remap(blockIdx.x, P.B * P.H, P.nqb) : xcd_remap(blockIdx.x, gridDim.x);
   const int i = blk % P.nqb, bh = blk / P.nqb;
   const int N = P.N;
   const int row0 = i * 128;
@@ -388,8 +390,12 @@ template <int BK>
 hipError_t launch(const Dims& P, const uint8_t* qc, const float* qs, const uint8_t* kc, const float* ks,
                   const uint8_t* vc, const float* vs, const uint32_t* vm, const int32_t* idx, const float* w,
                   const int32_t* cnt, void* out, float* lse, hipStream_t s) {
+  // gathered operands of one head: K codes, V codes (padded to whole sub-blocks) and
+  // the scaled V-Smooth means
+  const size_t head_bytes = size_t(P.N) * kD + size_t(P.nkb) * BK * kD + size_t(P.nkb) * kD * 4;
+  const int head_major = size_t(kXcds) * head_bytes > kMallBytes;
   hipLaunchKernelGGL((attn_fwd_fp8<BK>), dim3(P.B * P.H * P.nqb), dim3(256), 0, s, P, qc, qs, kc, ks, vc, vs, vm, idx,
-                     w, cnt, static_cast<uint16_t*>(out), lse);
+                     w, cnt, static_cast<uint16_t*>(out), lse, head_major);
   return hipGetLastError();
 }
 

@@ -544,14 +544,12 @@ __global__ __launch_bounds__(256) void attn_fwd_f32(Dims P, const float* __restr
   }
 }
 
-// Capacity of the Infinity Cache (MALL) that the XCDs share. When eight heads' K and
-// V (what eight XCDs on eight different heads read at once) exceed it, the query
-// blocks are taken head-major (xcd_head_remap); otherwise each XCD keeps one
-// contiguous range of query blocks (xcd_remap), the better order for its own L2.
-// Measured on one box, same inputs: 75600 tokens x 40 heads 9.65 -> 9.12 ms, 118800
-// x 24 heads 14.83 -> 13.63 ms; 32760 x 12 heads (all of K and V fit) 634 -> 644 us,
-// so it keeps the contiguous ranges.
-constexpr size_t kMallBytes = size_t(256) << 20;
+// When eight heads' K and V (what eight XCDs on eight different heads read at once)
+// exceed the Infinity Cache, the query blocks are taken head-major (xcd_head_remap);
+// otherwise each XCD keeps one contiguous range of query blocks (xcd_remap), the
+// better order for its own L2. Measured on one box, same inputs: 75600 tokens x 40
+// heads 9.65 -> 9.12 ms, 118800 x 24 heads 14.83 -> 13.63 ms; 32760 x 12 heads (all
+// of K and V fit) 634 -> 644 us, so it keeps the contiguous ranges.
 
 template <int D, int BQ, int BK>
 hipError_t launch_bf16(const Dims& P, const void* q, const void* k, const void* v, const int32_t* idx,
