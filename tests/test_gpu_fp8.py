@@ -183,7 +183,8 @@ def _lists(B, H, nqb, nkb, density, seed, empty_row=None):
     return idx, w, cnt
 
 
-def _check_attn(q, k, v, bk, density, seed, blocks=None, rows_per_block=None, empty_row=None, scale=0.0):
+def _check_attn(q, k, v, bk, density, seed, blocks=None, rows_per_block=None, empty_row=None, scale=0.0,
+                every_row_written=False):
     dev = _gpu()
     bq = 128
     qd, kd, vd = (x.to(dev) for x in (q, k, v))
@@ -191,9 +192,15 @@ def _check_attn(q, k, v, bk, density, seed, blocks=None, rows_per_block=None, em
     B, H, N, d = q.shape
     idx, w, cnt = _lists(B, H, desc.nqb, desc.nkb, density, seed, empty_row)
     ops = ab.ab_fp8_prepare(desc, qd, kd, vd)
+    out0 = lse0 = None
+    if every_row_written:  # outputs start as NaN: every row must be overwritten
+        out0 = torch.full((B, H, N, d), float("nan"), dtype=torch.bfloat16, device=dev)
+        lse0 = torch.full((B, H, N), float("nan"), dtype=torch.float32, device=dev)
     out, lse = ab.ab_attn_fwd_fp8(desc, ops, torch.from_numpy(idx).to(dev), torch.from_numpy(w).to(dev),
-                                  torch.from_numpy(cnt).to(dev))
+                                  torch.from_numpy(cnt).to(dev), out=out0, lse=lse0)
     torch.cuda.synchronize()
+    if every_row_written:
+        assert not torch.isnan(out).any() and not torch.isnan(lse).any()
     out = out.float().cpu().numpy()
     lse = lse.cpu().numpy()
     heads = [(b, h) for b in range(B) for h in range(H)] if blocks is None else sorted({(b, h) for (b, h, _) in blocks})
@@ -296,12 +303,14 @@ def test_fp8_random_configurations(cfg):
 def test_attn_fp8_video_shape(name):
     """Full sequence length of the workload (its first and last head), sampled blocks
     and rows: the wan1.3b shape (k_block 32, 1024 sub-blocks a row) and the
-    HunyuanVideo shape (k_block 16, 7425 sub-blocks a row, ragged tail)."""
+    HunyuanVideo shape (k_block 16, 7425 sub-blocks a row, ragged tail; eight heads'
+    FP8 operands exceed the Infinity Cache, so the kernel takes its query blocks
+    head-major). Every row of the output is written (it starts as NaN)."""
     w = workloads.get(name)
     q, k, v = _two_heads(name)
     nqb = -(-w.N // w.q_block)
     blocks = [(0, 0, 0), (0, 0, nqb - 1), (0, 1, 77), (0, 1, nqb - 1)]
-    _check_attn(q, k, v, w.k_block, w.density, seed=11, blocks=blocks, rows_per_block=6)
+    _check_attn(q, k, v, w.k_block, w.density, seed=11, blocks=blocks, rows_per_block=6, every_row_written=True)
 
 
 # ---- ab_attn_fwd_fp8 against the plain definition (one reference per row) -----------
