@@ -64,6 +64,11 @@ def parse_args():
     ap.add_argument("--fp8", action="store_true",
                     help="run the FP8 variant of the attention stage (ab_fp8_prepare + ab_attn_fwd_fp8: E4M3 "
                          "products, V-Smooth, ExpCast-FP8) instead of the bf16 kernel; not the headline line")
+    ap.add_argument("--attn-order", choices=("auto", "contiguous"), default="auto",
+                    help="order of the attention kernel's query blocks: auto = the kernel's own choice (head-major "
+                         "when eight heads' K and V exceed the Infinity Cache, else one contiguous range per XCD); "
+                         "contiguous = ab_attn_fwd_ordered with the identity order (one contiguous range per XCD "
+                         "always), for comparing the two; the outputs are the same")
     ap.add_argument("--graph", action="store_true",
                     help="replay one step captured in a HIP graph instead of launching the three calls eagerly "
                          "(measured: no faster, the launches already run ahead of the GPU)")
@@ -629,8 +634,14 @@ def main():
 
     stream = torch.cuda.current_stream()
     ev = {name: [] for name in ("score", "sample", "attn")}
+    ident = None
+    if args.attn_order == "contiguous":
+        ident = torch.arange(w.B * w.H * nqb, dtype=torch.int32, device=dev)
     fp8_ops = None
     if args.fp8:
+        if ident is not None:
+            print("--attn-order applies to the bf16 kernel only", file=sys.stderr)
+            sys.exit(2)
         if w.dtype != "bf16" or w.d != 128 or w.q_block != 128:
             print("--fp8 needs a bf16 workload with d = 128 and q_block = 128", file=sys.stderr)
             sys.exit(2)
@@ -648,7 +659,10 @@ def main():
         if record:
             e[2].record(stream)
         if fp8_ops is None:
-            ab.ab_attn_fwd(desc, qd, kd, vd, idx, wts, cnt, out=out, lse=lse)
+            if ident is None:
+                ab.ab_attn_fwd(desc, qd, kd, vd, idx, wts, cnt, out=out, lse=lse)
+            else:
+                ab.ab_attn_fwd_ordered(desc, qd, kd, vd, idx, wts, cnt, ident, out=out, lse=lse)
             if record:
                 e[3].record(stream)
         else:
@@ -761,6 +775,7 @@ def main():
             "stage_ms": stage_ms,
             "cold_cache": cold,
             "hip_graph": bool(args.graph),
+            "attn_order": args.attn_order,
             "attention_variant": "bf16" if fp8_ops is None else "fp8 (E4M3 QK and PV, V-Smooth, ExpCast-FP8)",
             "fp8_rel_l2_vs_bf16_path": fp8_vs_bf16,
             "attn_actual_tflops": achieved,
